@@ -1,0 +1,460 @@
+/*
+ * Plain CPU oracle for the gated delta rule recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+ * reference that the tests, the smoke check and the benchmark's CPU-baseline
+ * leg compare the HIP library against.  Nothing in the product path may link,
+ * load or call it, and it shares no source, header, table or helper with the
+ * HIP library.
+ *
+ * Sources (the four documentation pages the method is described on):
+ *   [fwd]    "gated_delta_recurrence_fwd_gpu" (Mojo kernel API page):
+ *            summary paragraph and Args (slot-indexed ragged forward).
+ *   [verify] "gated_delta_recurrence_verify_ring_gpu" (Mojo kernel API page):
+ *            summary paragraphs, Parameters (ring_dtype) and Args (ring).
+ *   [shape]  "gated_delta_recurrence_fwd_shape" (Mojo graph-op page).
+ *   [gdp]    "core.ssm.ops.gdp.fused_recurrent" (Megatron Core API page):
+ *            module summary, fused_recurrent_gated_delta_rule_update
+ *            parameters.
+ *
+ * The recurrence (per sequence and value head, a K x V state S carried token
+ * by token; the pages call it the gated delta rule and describe the state as
+ * "[K, V]" with a per-token decay factor and beta gate):
+ *     S  <- a_t * S                      (decay)
+ *     r  =  S^T k_t                      (retrieval, one value per V column)
+ *     u  =  beta_t * (v_t - r)           (delta correction)
+ *     S  <- S + k_t u^T                  (rank-1 write)
+ *     o_t = scale * S^T q_t              (read-out, after the write)
+ * with q_t and k_t optionally L2-normalised first, and scale defaulting to
+ * 1/sqrt(K).  Everything is written in this order, in float32 (the work dtype
+ * the fwd page fixes), one scalar operation at a time, with contraction off
+ * (built with -ffp-contract=off) so that no fused multiply-add appears.
+ *
+ * Readings of points the pages leave open (each one is listed with its reason
+ * in the design notes of this repository):
+ *   - L2 norm: x * (1 / sqrt(sum x^2 + eps)) with eps = 1e-6.
+ *   - GQA: value head hv reads key head hv / (nv / nk).
+ *   - bf16 state stores round to nearest even, once per store; loads widen.
+ *   - Slot index 0xFFFFFFFF (-1 as int32) is a padding request in every
+ *     entry: zero output, no state, ring or snapshot access.
+ *   - Ring record (verify page: "the record the fold needs"):
+ *       [ k_hat (K) | u of value head h*G+m, m < G (G*V) | a of those heads (G) ]
+ *     so the fold needs no norm, exp or reduction.
+ *   - Fold count: per-row accepted[b]; 0 or > RING_LEN leaves the state alone.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_L2NORM_EPS 1e-6f
+#define ORACLE_PAD_SLOT 0xFFFFFFFFu
+
+/* ---------------------------------------------------------------- bf16 --- */
+
+/* Round a float32 to bfloat16, nearest-even on the dropped 16 bits.  NaN stays
+ * a (quiet) NaN. */
+static uint16_t oracle_bf16_round(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, sizeof x);
+    if ((x & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((x >> 16) | 0x0040u);
+    uint32_t keep_lsb = (x >> 16) & 1u;
+    x += 0x7fffu + keep_lsb;
+    return (uint16_t)(x >> 16);
+}
+
+static float oracle_bf16_widen(uint16_t h)
+{
+    uint32_t x = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &x, sizeof f);
+    return f;
+}
+
+/* Exposed so the tests can pin the rounding against a library conversion. */
+void oracle_bf16_round_array(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_round(in[i]);
+}
+
+/* A K*V block of state in either float32 or bfloat16 storage. */
+static void oracle_load_block(const void* base, int bf16, int64_t offset, int64_t n, float* dst)
+{
+    if (bf16) {
+        const uint16_t* p = (const uint16_t*)base + offset;
+        for (int64_t i = 0; i < n; ++i)
+            dst[i] = oracle_bf16_widen(p[i]);
+    } else {
+        const float* p = (const float*)base + offset;
+        for (int64_t i = 0; i < n; ++i)
+            dst[i] = p[i];
+    }
+}
+
+static void oracle_store_block(void* base, int bf16, int64_t offset, int64_t n, const float* src)
+{
+    if (bf16) {
+        uint16_t* p = (uint16_t*)base + offset;
+        for (int64_t i = 0; i < n; ++i)
+            p[i] = oracle_bf16_round(src[i]);
+    } else {
+        float* p = (float*)base + offset;
+        for (int64_t i = 0; i < n; ++i)
+            p[i] = src[i];
+    }
+}
+
+/* ------------------------------------------------------------ one step --- */
+
+/* x_hat = x / sqrt(sum x^2 + eps), written as a multiply by the reciprocal
+ * root ([fwd] summary: the norm is a scalar factor). */
+static void oracle_l2norm(int n, const float* x, float* out)
+{
+    float sq = 0.0f;
+    for (int i = 0; i < n; ++i)
+        sq = sq + x[i] * x[i];
+    float rho = 1.0f / sqrtf(sq + ORACLE_L2NORM_EPS);
+    for (int i = 0; i < n; ++i)
+        out[i] = x[i] * rho;
+}
+
+/*
+ * One recurrence step on S (K rows, V columns, row-major, V fastest).
+ *   khat, qhat: the (already normalised, if enabled) key and query, length K.
+ *   v:          the value, length V.
+ *   a:          decay factor.
+ *   beta:       beta gate; a single value, or V values when beta_per_v.
+ *   o:          V outputs (scale * S^T qhat after the write), or NULL.
+ *   u_out:      receives u (V values) when not NULL.
+ */
+static void oracle_step(int K, int V, float* S, const float* khat, const float* qhat,
+                        const float* v, float a, const float* beta, int beta_per_v,
+                        float scale, float* o, float* u_out)
+{
+    float* u = (float*)malloc(sizeof(float) * (size_t)V);
+
+    for (int i = 0; i < K; ++i)
+        for (int j = 0; j < V; ++j)
+            S[i * V + j] = a * S[i * V + j];
+
+    for (int j = 0; j < V; ++j) {
+        float r = 0.0f;
+        for (int i = 0; i < K; ++i)
+            r = r + S[i * V + j] * khat[i];
+        float b = beta_per_v ? beta[j] : beta[0];
+        u[j] = b * (v[j] - r);
+    }
+
+    for (int i = 0; i < K; ++i)
+        for (int j = 0; j < V; ++j)
+            S[i * V + j] = S[i * V + j] + khat[i] * u[j];
+
+    if (o) {
+        for (int j = 0; j < V; ++j) {
+            float acc = 0.0f;
+            for (int i = 0; i < K; ++i)
+                acc = acc + S[i * V + j] * qhat[i];
+            o[j] = scale * acc;
+        }
+    }
+    if (u_out)
+        for (int j = 0; j < V; ++j)
+            u_out[j] = u[j];
+    free(u);
+}
+
+/* Fetch and optionally normalise q_t, k_t of key head h from the packed conv
+ * output row ([fwd] Args, qkv_conv_output: Q in channels [0, key_dim), K in
+ * [key_dim, 2*key_dim), V in [2*key_dim, 2*key_dim + value_dim)). */
+static void oracle_packed_qk(const float* row, int nk, int K, int h, int l2norm,
+                             float* qhat, float* khat)
+{
+    const float* q = row + (int64_t)h * K;
+    const float* k = row + (int64_t)nk * K + (int64_t)h * K;
+    if (l2norm) {
+        oracle_l2norm(K, q, qhat);
+        oracle_l2norm(K, k, khat);
+    } else {
+        for (int i = 0; i < K; ++i) {
+            qhat[i] = q[i];
+            khat[i] = k[i];
+        }
+    }
+}
+
+/* -------------------------------------------- ragged forward and verify --- */
+
+/*
+ * Shared walker for the [fwd] and [verify] entries.  All arrays contiguous:
+ *   row_offsets [B+1], slot_idx [B], qkv [T, 2*nk*K + nv*V],
+ *   decay, beta [T, nv], state [max_slots, nv, K, V], out [T, nv*V],
+ *   ring [ring_rows, nk, ring_len, rec_stride] (verify only), ring_slot_idx [B].
+ * Verify ([verify] summary): same outputs as the forward; a row no longer than
+ * ring_len writes one record per token and leaves the state alone; a longer
+ * row writes no record and stores its state like the forward.
+ */
+static int oracle_walk(int B, int nv, int nk, int K, int V, const uint32_t* row_offsets,
+                       const uint32_t* slot_idx, const float* qkv, const float* decay,
+                       const float* beta, int state_bf16, void* state, int64_t max_slots,
+                       float* out, float scale, int l2norm, float* ring,
+                       const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
+                       int64_t rec_stride)
+{
+    if (nk <= 0 || nv % nk != 0)
+        return -1;
+    const int G = nv / nk;
+    const int64_t conv_dim = 2 * (int64_t)nk * K + (int64_t)nv * V;
+    const int64_t kv = (int64_t)K * V;
+    float* S = (float*)malloc(sizeof(float) * (size_t)kv);
+    float* qhat = (float*)malloc(sizeof(float) * (size_t)K);
+    float* khat = (float*)malloc(sizeof(float) * (size_t)K);
+    float* u = (float*)malloc(sizeof(float) * (size_t)V);
+
+    for (int b = 0; b < B; ++b) {
+        const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];
+        const uint32_t slot = slot_idx[b];
+        for (int hv = 0; hv < nv; ++hv) {
+            const int h = hv / G;
+            const int m = hv % G;
+            if (slot == ORACLE_PAD_SLOT) {
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int j = 0; j < V; ++j)
+                        out[t * nv * V + (int64_t)hv * V + j] = 0.0f;
+                continue;
+            }
+            if ((int64_t)slot >= max_slots)
+                return -2;
+            const int64_t soff = ((int64_t)slot * nv + hv) * kv;
+            const int use_ring = ring != NULL && (t1 - t0) <= ring_len;
+            const uint32_t rrow = ring ? ring_slot_idx[b] : 0;
+            if (ring && use_ring && (int64_t)rrow >= ring_rows)
+                return -2;
+            oracle_load_block(state, state_bf16, soff, kv, S);
+            for (int64_t t = t0; t < t1; ++t) {
+                const float* row = qkv + t * conv_dim;
+                oracle_packed_qk(row, nk, K, h, l2norm, qhat, khat);
+                const float* v = row + 2 * (int64_t)nk * K + (int64_t)hv * V;
+                const float a = decay[t * nv + hv];
+                const float bt = beta[t * nv + hv];
+                oracle_step(K, V, S, khat, qhat, v, a, &bt, 0, scale,
+                            out + t * nv * V + (int64_t)hv * V, u);
+                if (use_ring) {
+                    float* rec = ring + (((int64_t)rrow * nk + h) * ring_len + (t - t0)) * rec_stride;
+                    if (m == 0)
+                        for (int i = 0; i < K; ++i)
+                            rec[i] = khat[i];
+                    for (int j = 0; j < V; ++j)
+                        rec[K + (int64_t)m * V + j] = u[j];
+                    rec[K + (int64_t)G * V + m] = a;
+                }
+            }
+            if (t1 > t0 && !use_ring)
+                oracle_store_block(state, state_bf16, soff, kv, S);
+        }
+    }
+    free(S);
+    free(qhat);
+    free(khat);
+    free(u);
+    return 0;
+}
+
+/* [fwd]: slot-indexed ragged forward; the state of slot slot_idx[b] is read,
+ * advanced over the row and written back in place. */
+int oracle_recurrence_fwd(int B, int nv, int nk, int K, int V, const uint32_t* row_offsets,
+                          const uint32_t* slot_idx, const float* qkv, const float* decay,
+                          const float* beta, int state_bf16, void* state, int64_t max_slots,
+                          float* out, float scale, int l2norm)
+{
+    return oracle_walk(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta, state_bf16,
+                       state, max_slots, out, scale, l2norm, NULL, NULL, 0, 0, 0);
+}
+
+/* [verify]: the forward over a verify window, recording a float32 ring. */
+int oracle_recurrence_verify_ring(int B, int nv, int nk, int K, int V,
+                                  const uint32_t* row_offsets, const uint32_t* slot_idx,
+                                  const float* qkv, const float* decay, const float* beta,
+                                  int state_bf16, void* state, int64_t max_slots, float* out,
+                                  float scale, int l2norm, float* ring,
+                                  const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
+                                  int64_t rec_stride)
+{
+    if (rec_stride < (int64_t)K + (int64_t)(nv / (nk > 0 ? nk : 1)) * (V + 1))
+        return -1;
+    return oracle_walk(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta, state_bf16,
+                       state, max_slots, out, scale, l2norm, ring, ring_slot_idx, ring_rows,
+                       ring_len, rec_stride);
+}
+
+/* [verify] (fold paragraphs): advance the live state of row b over its first
+ * accepted[b] ring records.  A count above ring_len (a row that committed in
+ * full during verify) or of zero leaves the state alone. */
+int oracle_state_fold(int B, int nv, int nk, int K, int V, const uint32_t* slot_idx,
+                      int state_bf16, void* state, int64_t max_slots, const float* ring,
+                      const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
+                      int64_t rec_stride, const uint32_t* accepted)
+{
+    if (nk <= 0 || nv % nk != 0)
+        return -1;
+    const int G = nv / nk;
+    const int64_t kv = (int64_t)K * V;
+    float* S = (float*)malloc(sizeof(float) * (size_t)kv);
+    for (int b = 0; b < B; ++b) {
+        const uint32_t n = accepted[b];
+        const uint32_t slot = slot_idx[b];
+        if (n == 0 || n > (uint32_t)ring_len || slot == ORACLE_PAD_SLOT)
+            continue;
+        if ((int64_t)slot >= max_slots || (int64_t)ring_slot_idx[b] >= ring_rows) {
+            free(S);
+            return -2;
+        }
+        for (int hv = 0; hv < nv; ++hv) {
+            const int h = hv / G, m = hv % G;
+            const int64_t soff = ((int64_t)slot * nv + hv) * kv;
+            oracle_load_block(state, state_bf16, soff, kv, S);
+            for (uint32_t t = 0; t < n; ++t) {
+                const float* rec =
+                    ring + (((int64_t)ring_slot_idx[b] * nk + h) * ring_len + t) * rec_stride;
+                const float* khat = rec;
+                const float* u = rec + K + (int64_t)m * V;
+                const float a = rec[K + (int64_t)G * V + m];
+                for (int i = 0; i < K; ++i)
+                    for (int j = 0; j < V; ++j)
+                        S[i * V + j] = a * S[i * V + j];
+                for (int i = 0; i < K; ++i)
+                    for (int j = 0; j < V; ++j)
+                        S[i * V + j] = S[i * V + j] + khat[i] * u[j];
+            }
+            oracle_store_block(state, state_bf16, soff, kv, S);
+        }
+    }
+    free(S);
+    return 0;
+}
+
+/* ----------------------------------------------------- fused update ------ */
+
+/*
+ * [gdp] fused_recurrent_gated_delta_rule_update, all arrays contiguous:
+ *   q, k [B, T, H, K]; v, o [B, T, HV, V]; g [B, T, HV] log decays or NULL
+ *   (no decay); beta [B, T, HV] or [B, T, HV, V] (beta_per_v) or NULL (1).
+ *   cu_seqlens [N+1] or NULL: with it B must be 1 and sequence n spans
+ *   [cu_seqlens[n], cu_seqlens[n+1]) of the T axis; without it N = B and every
+ *   sequence has T tokens.
+ *   state [num_slots, HV, K, V] with state_indices [N] (-1 = padding: zero
+ *   output, nothing else touched), or NULL; then initial_state [N, HV, K, V]
+ *   (NULL = zeros) seeds the walk and final_state [N, HV, K, V] (or NULL)
+ *   receives the end state.
+ *   intermediate [num_slots, int_tokens, HV, K, V] or NULL: entry [slot, i]
+ *   receives the state after draft token i, i.e. after (i+1)*steps_per_token
+ *   steps of the sequence; needs state.  All state-like buffers share one
+ *   storage dtype (state_bf16).
+ */
+int oracle_fused_recurrent_update(int B, int T, int H, int HV, int K, int V, const float* q,
+                                  const float* k, const float* v, const float* g,
+                                  const float* beta, int beta_per_v, float scale, int l2norm,
+                                  const int32_t* cu_seqlens, int N, int state_bf16, void* state,
+                                  int64_t num_slots, const int32_t* state_indices,
+                                  const void* initial_state, void* final_state,
+                                  void* intermediate, int64_t int_tokens, int steps_per_token,
+                                  float* o)
+{
+    if (H <= 0 || HV % H != 0)
+        return -1;
+    if (cu_seqlens && B != 1)
+        return -1;
+    if (!cu_seqlens)
+        N = B;
+    if (intermediate && (!state || steps_per_token < 1))
+        return -1;
+    const int G = HV / H;
+    const int64_t kv = (int64_t)K * V;
+    float* S = (float*)malloc(sizeof(float) * (size_t)kv);
+    float* qhat = (float*)malloc(sizeof(float) * (size_t)K);
+    float* khat = (float*)malloc(sizeof(float) * (size_t)K);
+
+    for (int n = 0; n < N; ++n) {
+        /* flat token range on the (B*T) axis */
+        int64_t f0, f1;
+        if (cu_seqlens) {
+            f0 = cu_seqlens[n];
+            f1 = cu_seqlens[n + 1];
+        } else {
+            f0 = (int64_t)n * T;
+            f1 = f0 + T;
+        }
+        int32_t idx = state_indices ? state_indices[n] : n;
+        for (int hv = 0; hv < HV; ++hv) {
+            const int h = hv / G;
+            if (state && state_indices && idx < 0) {
+                for (int64_t f = f0; f < f1; ++f)
+                    for (int j = 0; j < V; ++j)
+                        o[(f * HV + hv) * V + j] = 0.0f;
+                continue;
+            }
+            if (state && (int64_t)idx >= num_slots) {
+                free(S);
+                free(qhat);
+                free(khat);
+                return -2;
+            }
+            if (state)
+                oracle_load_block(state, state_bf16, ((int64_t)idx * HV + hv) * kv, kv, S);
+            else if (initial_state)
+                oracle_load_block(initial_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);
+            else
+                for (int64_t e = 0; e < kv; ++e)
+                    S[e] = 0.0f;
+
+            for (int64_t f = f0; f < f1; ++f) {
+                const float* qt = q + (f * H + h) * K;
+                const float* kt = k + (f * H + h) * K;
+                if (l2norm) {
+                    oracle_l2norm(K, qt, qhat);
+                    oracle_l2norm(K, kt, khat);
+                } else {
+                    for (int i = 0; i < K; ++i) {
+                        qhat[i] = qt[i];
+                        khat[i] = kt[i];
+                    }
+                }
+                const float a = g ? expf(g[f * HV + hv]) : 1.0f;
+                float one = 1.0f;
+                const float* bt = &one;
+                int per_v = 0;
+                if (beta) {
+                    bt = beta_per_v ? beta + (f * HV + hv) * V : beta + (f * HV + hv);
+                    per_v = beta_per_v;
+                }
+                oracle_step(K, V, S, khat, qhat, v + (f * HV + hv) * V, a, bt, per_v, scale,
+                            o + (f * HV + hv) * V, NULL);
+                const int64_t step = f - f0 + 1;
+                if (intermediate && step % steps_per_token == 0) {
+                    const int64_t i = step / steps_per_token - 1;
+                    if (i < int_tokens)
+                        oracle_store_block(intermediate, state_bf16,
+                                           (((int64_t)idx * int_tokens + i) * HV + hv) * kv, kv,
+                                           S);
+                }
+            }
+            if (state)
+                oracle_store_block(state, state_bf16, ((int64_t)idx * HV + hv) * kv, kv, S);
+            else if (final_state)
+                oracle_store_block(final_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);
+        }
+    }
+    free(S);
+    free(qhat);
+    free(khat);
+    return 0;
+}
+
+/* [shape]: the forward's output is [total_seq_len, num_value_heads * V]. */
+void oracle_fwd_output_shape(int64_t total_seq_len, int64_t nv, int64_t V, int64_t out[2])
+{
+    out[0] = total_seq_len;
+    out[1] = nv * V;
+}

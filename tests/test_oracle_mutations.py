@@ -1,0 +1,57 @@
+"""Plant plausible mistakes in copies of the oracle and check that each one
+trips at least one pin (CPU only; the real oracle is never modified)."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gdr_oracle.c")
+
+# (name, original text, planted text)
+MUTATIONS = [
+    ("delta_sign", "u[j] = b * (v[j] - r);", "u[j] = b * (v[j] + r);"),
+    ("beta_on_r_only", "u[j] = b * (v[j] - r);", "u[j] = v[j] - b * r;"),
+    ("no_decay", "S[i * V + j] = a * S[i * V + j];", "S[i * V + j] = S[i * V + j];"),
+    ("retrieval_transposed", "r = r + S[i * V + j] * khat[i];", "r = r + S[j * V + i] * khat[i];"),
+    ("readout_with_k", "acc = acc + S[i * V + j] * qhat[i];", "acc = acc + S[i * V + j] * khat[i];"),
+    ("write_v_not_u", "S[i * V + j] = S[i * V + j] + khat[i] * u[j];",
+     "S[i * V + j] = S[i * V + j] + khat[i] * v[j];"),
+    ("no_scale", "o[j] = scale * acc;", "o[j] = acc;"),
+    ("gqa_modulo", "const int h = hv / G;", "const int h = hv % nk;"),
+    ("norm_no_sqrt", "float rho = 1.0f / sqrtf(sq + ORACLE_L2NORM_EPS);",
+     "float rho = 1.0f / (sq + ORACLE_L2NORM_EPS);"),
+    ("bf16_truncate", "x += 0x7fffu + keep_lsb;", "x += 0u * keep_lsb;"),
+    ("fold_wrong_head_a", "const float a = rec[K + (int64_t)G * V + m];",
+     "const float a = rec[K + (int64_t)G * V];"),
+    ("snapshot_off_by_one", "const int64_t i = step / steps_per_token - 1;",
+     "const int64_t i = step / steps_per_token;"),
+    ("padding_not_zero", "o[(f * HV + hv) * V + j] = 0.0f;", "o[(f * HV + hv) * V + j] = 1.0f;"),
+    ("long_row_not_committed", "if (t1 > t0 && !use_ring)", "if (t1 > t0 && ring == NULL)"),
+    ("offsets_shifted", "const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];",
+     "const int64_t t0 = row_offsets[b] + (b > 0), t1 = row_offsets[b + 1];"),
+]
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, orig, planted, tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    assert orig in text, f"mutation site for {name} no longer exists in the oracle"
+    mutant = os.path.join(tmp_path, f"{name}.c")
+    with open(mutant, "w") as f:
+        f.write(text.replace(orig, planted, 1))  # first site: the step itself
+    lib = os.path.join(tmp_path, f"lib{name}.so")
+    subprocess.run(["gcc", *oracle_build.CFLAGS, mutant, "-o", lib, "-lm"], check=True)
+    failed = []
+    with oracle.using_library(lib):
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError):
+                failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
