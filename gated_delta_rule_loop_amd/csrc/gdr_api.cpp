@@ -1,0 +1,500 @@
+// Host side of the C ABI declared in include/gdr.h: argument validation,
+// launch-shape choice and dispatch to the gfx950 kernels.  Nothing here
+// allocates, frees or synchronises device memory.
+#include "gdr.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gdr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+bool present(const gdr_tensor* t) { return t != nullptr && t->data != nullptr; }
+
+const char* dtype_name(int32_t d) {
+    switch (d) {
+        case GDR_DTYPE_F32: return "f32";
+        case GDR_DTYPE_BF16: return "bf16";
+        case GDR_DTYPE_U32: return "u32";
+        case GDR_DTYPE_I32: return "i32";
+        default: return "?";
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Rank, dtype and exact shape check; a shape entry < 0 matches anything.
+int check_tensor(const char* fn, const char* name, const gdr_tensor* t, int ndim,
+                 const int64_t* shape, bool allow_f32, bool allow_bf16, bool allow_idx) {
+    if (!present(t)) return fail(GDR_ERR_INVALID_ARG, "%s: %s is null", fn, name);
+    if (t->ndim != ndim)
+        return fail(GDR_ERR_INVALID_ARG, "%s: %s must have rank %d (got %d)", fn, name, ndim,
+                    t->ndim);
+    const bool ok = (allow_f32 && t->dtype == GDR_DTYPE_F32) ||
+                    (allow_bf16 && t->dtype == GDR_DTYPE_BF16) ||
+                    (allow_idx && (t->dtype == GDR_DTYPE_U32 || t->dtype == GDR_DTYPE_I32));
+    if (!ok)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s has unsupported dtype %s", fn, name,
+                    dtype_name(t->dtype));
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] < 0)
+            return fail(GDR_ERR_INVALID_ARG, "%s: %s has a negative extent", fn, name);
+        if (shape && shape[i] >= 0 && t->shape[i] != shape[i])
+            return fail(GDR_ERR_INVALID_ARG, "%s: %s dim %d is %lld, expected %lld", fn, name, i,
+                        static_cast<long long>(t->shape[i]), static_cast<long long>(shape[i]));
+    }
+    return GDR_OK;
+}
+
+// Innermost stride 1, 16-byte base, outer strides multiples of `mult`.
+int check_layout(const char* fn, const char* name, const gdr_tensor* t, int64_t mult) {
+    if (t->stride[t->ndim - 1] != 1)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s must have unit innermost stride", fn, name);
+    if (!aligned16(t->data))
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s base must be 16-byte aligned", fn, name);
+    for (int i = 0; i < t->ndim - 1; ++i)
+        if (t->stride[i] % mult != 0)
+            return fail(GDR_ERR_UNSUPPORTED, "%s: %s stride %d must be a multiple of %lld", fn,
+                        name, i, static_cast<long long>(mult));
+    return GDR_OK;
+}
+
+int check_index_vec(const char* fn, const char* name, const gdr_tensor* t, int64_t n) {
+    const int64_t shape[1] = {n};
+    int rc = check_tensor(fn, name, t, 1, shape, false, false, true);
+    if (rc) return rc;
+    if (n > 1 && t->stride[0] != 1)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s must be contiguous", fn, name);
+    return GDR_OK;
+}
+
+bool head_dim_built(int64_t K) { return K == 16 || K == 32 || K == 64 || K == 128; }
+
+// State-like tensor [slots, nv, K, V] with a dense K x V block per head.
+int check_state(const char* fn, const char* name, const gdr_tensor* t, int ndim,
+                const int64_t* shape) {
+    int rc = check_tensor(fn, name, t, ndim, shape, true, true, false);
+    if (rc) return rc;
+    const int64_t K = t->shape[ndim - 2], V = t->shape[ndim - 1];
+    if (K != V) return fail(GDR_ERR_UNSUPPORTED, "%s: %s needs K == V", fn, name);
+    if (!head_dim_built(K))
+        return fail(GDR_ERR_UNSUPPORTED, "%s: head dim %lld not built (16, 32, 64, 128)", fn,
+                    static_cast<long long>(K));
+    if (t->stride[ndim - 1] != 1 || t->stride[ndim - 2] != V)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s needs a dense K x V block per head", fn, name);
+    return check_layout(fn, name, t, t->dtype == GDR_DTYPE_BF16 ? 8 : 4);
+}
+
+float resolve_scale(float scale, int64_t K) {
+    if (!(scale > 0.0f)) return 1.0f / std::sqrt(static_cast<float>(K));
+    return scale;
+}
+
+// Launch shape: few tokens per row -> wide column tiles (16-byte bf16 state
+// loads, one token per stage); long rows -> narrow tiles (more waves for the
+// token-serial chain) and 16-token stages.  The reduction order does not
+// depend on this choice.
+gdr::LaunchShape pick_shape(int64_t K, int64_t G, int64_t total_tokens, int64_t rows) {
+    gdr::LaunchShape s{};
+    s.K = static_cast<int>(K);
+    const bool long_rows = rows > 0 && total_tokens >= 16 * rows;
+    if (long_rows) {
+        s.cpl = 2;
+        s.chunk = 16;
+    } else {
+        s.cpl = K == 128 ? 4 : (K == 64 ? 8 : (K == 32 ? 4 : 2));
+        s.chunk = 8;
+    }
+    const int64_t tiles = K / (gdr::kLanesPerRow * s.cpl);
+    const int64_t units = G * tiles;
+    s.wpg = units % 4 == 0 ? 4 : (units % 2 == 0 ? 2 : 1);
+    return s;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess)
+        return fail(GDR_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    g_last_error.clear();
+    return GDR_OK;
+}
+
+const uint32_t* as_u32(const gdr_tensor* t) {
+    return present(t) ? static_cast<const uint32_t*>(t->data) : nullptr;
+}
+
+// Shared by the forward and the verify entry points.
+int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
+                const gdr_tensor* state, const gdr_tensor* slot_idx, const gdr_tensor* qkv,
+                const gdr_tensor* decay, const gdr_tensor* beta, const gdr_tensor* offsets,
+                const gdr_tensor* ring, const gdr_tensor* ring_slot_idx, float scale,
+                uint32_t flags, void* stream) {
+    if (nk < 1 || nv < nk || nv % nk != 0)
+        return fail(GDR_ERR_INVALID_ARG, "%s: num_value_heads (%d) must be a positive multiple "
+                    "of num_key_heads (%d)", fn, nv, nk);
+    if (flags & ~GDR_FLAG_L2NORM_QK)
+        return fail(GDR_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+    int rc;
+    const int64_t st_shape[4] = {-1, nv, -1, -1};
+    if ((rc = check_state(fn, "recurrent_state", state, 4, st_shape))) return rc;
+    const int64_t K = state->shape[2], V = state->shape[3];
+    if (!present(slot_idx)) return fail(GDR_ERR_INVALID_ARG, "%s: slot_idx is null", fn);
+    const int64_t B = slot_idx->shape[0];
+    if ((rc = check_index_vec(fn, "slot_idx", slot_idx, B))) return rc;
+    if ((rc = check_index_vec(fn, "input_row_offsets", offsets, B + 1))) return rc;
+    const int64_t conv = 2 * nk * K + nv * V;
+    const int64_t qkv_shape[2] = {-1, conv};
+    if ((rc = check_tensor(fn, "qkv_conv_output", qkv, 2, qkv_shape, true, false, false)))
+        return rc;
+    if ((rc = check_layout(fn, "qkv_conv_output", qkv, 4))) return rc;
+    const int64_t T = qkv->shape[0];
+    const int64_t gate_shape[2] = {T, nv};
+    if ((rc = check_tensor(fn, "decay_per_token", decay, 2, gate_shape, true, false, false)))
+        return rc;
+    if ((rc = check_tensor(fn, "beta_per_token", beta, 2, gate_shape, true, false, false)))
+        return rc;
+    const int64_t out_shape[2] = {T, nv * V};
+    if ((rc = check_tensor(fn, "recurrence_output", out, 2, out_shape, true, false, false)))
+        return rc;
+    if ((rc = check_layout(fn, "recurrence_output", out, 4))) return rc;
+    const int64_t G = nv / nk;
+
+    gdr::RecParams p{};
+    if (ring) {
+        if ((rc = check_tensor(fn, "ring", ring, 4, nullptr, true, false, false))) return rc;
+        if (ring->shape[1] != nk)
+            return fail(GDR_ERR_INVALID_ARG, "%s: ring dim 1 must be num_key_heads", fn);
+        if (ring->shape[2] < 1)
+            return fail(GDR_ERR_INVALID_ARG, "%s: ring length must be >= 1", fn);
+        if (ring->shape[3] < gdr_ring_record_elements(static_cast<int32_t>(G),
+                                                      static_cast<int32_t>(K),
+                                                      static_cast<int32_t>(V)))
+            return fail(GDR_ERR_INVALID_ARG, "%s: ring record stride %lld below %lld", fn,
+                        static_cast<long long>(ring->shape[3]),
+                        static_cast<long long>(gdr_ring_record_elements(
+                            static_cast<int32_t>(G), static_cast<int32_t>(K),
+                            static_cast<int32_t>(V))));
+        if ((rc = check_layout(fn, "ring", ring, 4))) return rc;
+        if ((rc = check_index_vec(fn, "ring_slot_idx", ring_slot_idx, B))) return rc;
+        p.ring = static_cast<float*>(ring->data);
+        p.ring_idx = as_u32(ring_slot_idx);
+        p.ring_row = ring->stride[0];
+        p.ring_head = ring->stride[1];
+        p.ring_tok = ring->stride[2];
+        p.ring_len = static_cast<int32_t>(ring->shape[2]);
+    }
+    if (B == 0) {
+        g_last_error.clear();
+        return GDR_OK;
+    }
+    if (B * nk > (int64_t{1} << 28))
+        return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
+
+    const gdr::LaunchShape s = pick_shape(K, G, T, B);
+    const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
+    p.rows = static_cast<int32_t>(B);
+    p.nv = nv;
+    p.nk = nk;
+    p.G = static_cast<int32_t>(G);
+    p.parts = static_cast<int32_t>(units / s.wpg);
+    p.offsets = as_u32(offsets);
+    const float* x = static_cast<const float*>(qkv->data);
+    const int64_t ch = qkv->stride[1];
+    p.q = x;
+    p.k = x + nk * K * ch;
+    p.v = x + 2 * nk * K * ch;
+    p.q_tok = p.k_tok = p.v_tok = qkv->stride[0];
+    p.q_head = p.k_head = K;
+    p.v_head = V;
+    p.gate = static_cast<const float*>(decay->data);
+    p.g_tok = decay->stride[0];
+    p.g_head = decay->stride[1];
+    p.gate_is_log = 0;
+    p.beta = static_cast<const float*>(beta->data);
+    p.b_tok = beta->stride[0];
+    p.b_head = beta->stride[1];
+    p.out = static_cast<float*>(out->data);
+    p.o_tok = out->stride[0];
+    p.o_head = V;
+    p.slot_idx = as_u32(slot_idx);
+    p.src = state->data;
+    p.src_slot = state->stride[0];
+    p.src_head = state->stride[1];
+    p.src_by_slot = 1;
+    p.dst = state->data;
+    p.dst_slot = state->stride[0];
+    p.dst_head = state->stride[1];
+    p.dst_by_slot = 1;
+    p.spt = 1;
+    p.scale = resolve_scale(scale, K);
+    p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
+    const gdr::StateType st =
+        state->dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
+    return hip_status(fn, gdr::launch_recurrence(p, s, st, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_recurrence_fwd(int32_t num_value_heads, int32_t num_key_heads,
+                       const gdr_tensor* recurrence_output, const gdr_tensor* recurrent_state,
+                       const gdr_tensor* slot_idx, const gdr_tensor* qkv_conv_output,
+                       const gdr_tensor* decay_per_token, const gdr_tensor* beta_per_token,
+                       const gdr_tensor* input_row_offsets, float scale, uint32_t flags,
+                       void* stream) {
+    return packed_walk("gdr_recurrence_fwd", num_value_heads, num_key_heads, recurrence_output,
+                       recurrent_state, slot_idx, qkv_conv_output, decay_per_token,
+                       beta_per_token, input_row_offsets, nullptr, nullptr, scale, flags,
+                       stream);
+}
+
+int gdr_recurrence_verify_ring(int32_t num_value_heads, int32_t num_key_heads,
+                               const gdr_tensor* recurrence_output,
+                               const gdr_tensor* recurrent_state, const gdr_tensor* slot_idx,
+                               const gdr_tensor* qkv_conv_output,
+                               const gdr_tensor* decay_per_token,
+                               const gdr_tensor* beta_per_token,
+                               const gdr_tensor* input_row_offsets, const gdr_tensor* ring,
+                               const gdr_tensor* ring_slot_idx, float scale, uint32_t flags,
+                               void* stream) {
+    const char* fn = "gdr_recurrence_verify_ring";
+    if (!present(ring)) return fail(GDR_ERR_INVALID_ARG, "%s: ring is null", fn);
+    return packed_walk(fn, num_value_heads, num_key_heads, recurrence_output, recurrent_state,
+                       slot_idx, qkv_conv_output, decay_per_token, beta_per_token,
+                       input_row_offsets, ring, ring_slot_idx, scale, flags, stream);
+}
+
+int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
+                   const gdr_tensor* recurrent_state, const gdr_tensor* slot_idx,
+                   const gdr_tensor* ring, const gdr_tensor* ring_slot_idx,
+                   const gdr_tensor* accepted, void* stream) {
+    const char* fn = "gdr_state_fold";
+    const int32_t nv = num_value_heads, nk = num_key_heads;
+    if (nk < 1 || nv < nk || nv % nk != 0)
+        return fail(GDR_ERR_INVALID_ARG, "%s: num_value_heads (%d) must be a positive multiple "
+                    "of num_key_heads (%d)", fn, nv, nk);
+    int rc;
+    const int64_t st_shape[4] = {-1, nv, -1, -1};
+    if ((rc = check_state(fn, "recurrent_state", recurrent_state, 4, st_shape))) return rc;
+    const int64_t K = recurrent_state->shape[2], V = recurrent_state->shape[3];
+    if (!present(slot_idx)) return fail(GDR_ERR_INVALID_ARG, "%s: slot_idx is null", fn);
+    const int64_t B = slot_idx->shape[0];
+    if ((rc = check_index_vec(fn, "slot_idx", slot_idx, B))) return rc;
+    if ((rc = check_index_vec(fn, "ring_slot_idx", ring_slot_idx, B))) return rc;
+    if ((rc = check_index_vec(fn, "accepted", accepted, B))) return rc;
+    if ((rc = check_tensor(fn, "ring", ring, 4, nullptr, true, false, false))) return rc;
+    const int64_t G = nv / nk;
+    if (ring->shape[1] != nk)
+        return fail(GDR_ERR_INVALID_ARG, "%s: ring dim 1 must be num_key_heads", fn);
+    if (ring->shape[2] < 1) return fail(GDR_ERR_INVALID_ARG, "%s: ring length must be >= 1", fn);
+    if (ring->shape[3] < gdr_ring_record_elements(static_cast<int32_t>(G),
+                                                  static_cast<int32_t>(K),
+                                                  static_cast<int32_t>(V)))
+        return fail(GDR_ERR_INVALID_ARG, "%s: ring record stride too small", fn);
+    if ((rc = check_layout(fn, "ring", ring, 4))) return rc;
+    if (B == 0) {
+        g_last_error.clear();
+        return GDR_OK;
+    }
+    gdr::LaunchShape s = pick_shape(K, G, B, B);  // wide tiles
+    const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
+    gdr::FoldParams p{};
+    p.rows = static_cast<int32_t>(B);
+    p.nv = nv;
+    p.nk = nk;
+    p.G = static_cast<int32_t>(G);
+    p.parts = static_cast<int32_t>(units / s.wpg);
+    p.slot_idx = as_u32(slot_idx);
+    p.state = recurrent_state->data;
+    p.st_slot = recurrent_state->stride[0];
+    p.st_head = recurrent_state->stride[1];
+    p.ring = static_cast<const float*>(ring->data);
+    p.ring_idx = as_u32(ring_slot_idx);
+    p.ring_row = ring->stride[0];
+    p.ring_head = ring->stride[1];
+    p.ring_tok = ring->stride[2];
+    p.ring_len = static_cast<int32_t>(ring->shape[2]);
+    p.accepted = as_u32(accepted);
+    const gdr::StateType st =
+        recurrent_state->dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
+    return hip_status(fn, gdr::launch_fold(p, s, st, static_cast<hipStream_t>(stream)));
+}
+
+int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const gdr_tensor* v,
+                               const gdr_tensor* g, const gdr_tensor* beta, float scale,
+                               const gdr_tensor* initial_state, const gdr_tensor* final_state,
+                               uint32_t flags, const gdr_tensor* cu_seqlens,
+                               const gdr_tensor* state, const gdr_tensor* state_indices,
+                               const gdr_tensor* intermediate_states, int32_t steps_per_token,
+                               const gdr_tensor* o, void* stream) {
+    const char* fn = "gdr_fused_recurrent_update";
+    int rc;
+    if (flags & ~GDR_FLAG_L2NORM_QK)
+        return fail(GDR_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+    if ((rc = check_tensor(fn, "q", q, 4, nullptr, true, false, false))) return rc;
+    const int64_t B = q->shape[0], T = q->shape[1], H = q->shape[2], K = q->shape[3];
+    if ((rc = check_tensor(fn, "k", k, 4, q->shape, true, false, false))) return rc;
+    if ((rc = check_tensor(fn, "v", v, 4, nullptr, true, false, false))) return rc;
+    const int64_t HV = v->shape[2], V = v->shape[3];
+    if (v->shape[0] != B || v->shape[1] != T)
+        return fail(GDR_ERR_INVALID_ARG, "%s: v must be [B, T, HV, V] like q", fn);
+    if (H < 1 || HV < H || HV % H != 0)
+        return fail(GDR_ERR_INVALID_ARG, "%s: HV must be a positive multiple of H", fn);
+    if (K != V) return fail(GDR_ERR_UNSUPPORTED, "%s: K != V is not built", fn);
+    if (!head_dim_built(K))
+        return fail(GDR_ERR_UNSUPPORTED, "%s: head dim %lld not built (16, 32, 64, 128)", fn,
+                    static_cast<long long>(K));
+    if ((rc = check_layout(fn, "q", q, 1)) || (rc = check_layout(fn, "k", k, 1)) ||
+        (rc = check_layout(fn, "v", v, 4)))
+        return rc;
+    const int64_t gshape[3] = {B, T, HV};
+    if (present(g) && (rc = check_tensor(fn, "g", g, 3, gshape, true, false, false))) return rc;
+    if (present(beta)) {
+        if (beta->ndim == 4)
+            return fail(GDR_ERR_UNSUPPORTED, "%s: per-V-element beta is not built", fn);
+        if ((rc = check_tensor(fn, "beta", beta, 3, gshape, true, false, false))) return rc;
+    }
+    const int64_t oshape[4] = {B, T, HV, V};
+    if ((rc = check_tensor(fn, "o", o, 4, oshape, true, false, false))) return rc;
+    if ((rc = check_layout(fn, "o", o, 4))) return rc;
+
+    int64_t N = B;
+    if (present(cu_seqlens)) {
+        if (B != 1) return fail(GDR_ERR_INVALID_ARG, "%s: cu_seqlens needs B == 1", fn);
+        N = cu_seqlens->shape[0] - 1;
+        if (N < 0) return fail(GDR_ERR_INVALID_ARG, "%s: cu_seqlens is empty", fn);
+        if ((rc = check_index_vec(fn, "cu_seqlens", cu_seqlens, N + 1))) return rc;
+    }
+    if (steps_per_token < 1)
+        return fail(GDR_ERR_INVALID_ARG, "%s: steps_per_token must be >= 1", fn);
+
+    gdr::RecParams p{};
+    int32_t st_dtype = -1;
+    if (present(state)) {
+        const int64_t sshape[4] = {-1, HV, K, V};
+        if ((rc = check_state(fn, "state", state, 4, sshape))) return rc;
+        st_dtype = state->dtype;
+        p.src = p.dst = state->data;
+        p.src_slot = p.dst_slot = state->stride[0];
+        p.src_head = p.dst_head = state->stride[1];
+        p.src_by_slot = p.dst_by_slot = 1;
+        if (present(state_indices)) {
+            if ((rc = check_index_vec(fn, "state_indices", state_indices, N))) return rc;
+            p.slot_idx = as_u32(state_indices);
+        } else if (N > state->shape[0]) {
+            return fail(GDR_ERR_INVALID_ARG, "%s: state has fewer slots than sequences", fn);
+        }
+        if (present(intermediate_states)) {
+            const int64_t ishape[5] = {state->shape[0], -1, HV, K, V};
+            if ((rc = check_state(fn, "intermediate_states", intermediate_states, 5, ishape)))
+                return rc;
+            if (intermediate_states->dtype != st_dtype)
+                return fail(GDR_ERR_UNSUPPORTED, "%s: intermediate_states must match the state "
+                            "dtype", fn);
+            p.snap = intermediate_states->data;
+            p.snap_slot = intermediate_states->stride[0];
+            p.snap_tok = intermediate_states->stride[1];
+            p.snap_head = intermediate_states->stride[2];
+            p.snap_count = static_cast<int32_t>(intermediate_states->shape[1]);
+        }
+    } else {
+        if (present(intermediate_states))
+            return fail(GDR_ERR_INVALID_ARG, "%s: intermediate_states needs state", fn);
+        const int64_t dshape[4] = {N, HV, K, V};
+        if (present(initial_state)) {
+            if ((rc = check_state(fn, "initial_state", initial_state, 4, dshape))) return rc;
+            st_dtype = initial_state->dtype;
+            p.src = initial_state->data;
+            p.src_slot = initial_state->stride[0];
+            p.src_head = initial_state->stride[1];
+        }
+        if (present(final_state)) {
+            if ((rc = check_state(fn, "final_state", final_state, 4, dshape))) return rc;
+            if (st_dtype >= 0 && final_state->dtype != st_dtype)
+                return fail(GDR_ERR_UNSUPPORTED, "%s: initial and final state dtypes differ", fn);
+            st_dtype = final_state->dtype;
+            p.dst = final_state->data;
+            p.dst_slot = final_state->stride[0];
+            p.dst_head = final_state->stride[1];
+        }
+    }
+    if (N == 0 || (T == 0 && !present(cu_seqlens))) {
+        g_last_error.clear();
+        return GDR_OK;
+    }
+    if (N * H > (int64_t{1} << 28)) return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
+
+    const int64_t G = HV / H;
+    const gdr::LaunchShape s = pick_shape(K, G, B * T, N);
+    const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
+    p.rows = static_cast<int32_t>(N);
+    p.nv = static_cast<int32_t>(HV);
+    p.nk = static_cast<int32_t>(H);
+    p.G = static_cast<int32_t>(G);
+    p.parts = static_cast<int32_t>(units / s.wpg);
+    p.dense_len = static_cast<int32_t>(T);
+    p.offsets = as_u32(cu_seqlens);
+    p.q = static_cast<const float*>(q->data);
+    p.q_seq = q->stride[0]; p.q_tok = q->stride[1]; p.q_head = q->stride[2];
+    p.k = static_cast<const float*>(k->data);
+    p.k_seq = k->stride[0]; p.k_tok = k->stride[1]; p.k_head = k->stride[2];
+    p.v = static_cast<const float*>(v->data);
+    p.v_seq = v->stride[0]; p.v_tok = v->stride[1]; p.v_head = v->stride[2];
+    if (present(g)) {
+        p.gate = static_cast<const float*>(g->data);
+        p.g_seq = g->stride[0]; p.g_tok = g->stride[1]; p.g_head = g->stride[2];
+        p.gate_is_log = 1;
+    }
+    if (present(beta)) {
+        p.beta = static_cast<const float*>(beta->data);
+        p.b_seq = beta->stride[0]; p.b_tok = beta->stride[1]; p.b_head = beta->stride[2];
+    }
+    p.out = static_cast<float*>(o->data);
+    p.o_seq = o->stride[0]; p.o_tok = o->stride[1]; p.o_head = o->stride[2];
+    p.spt = steps_per_token;
+    p.scale = resolve_scale(scale, K);
+    p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
+    const gdr::StateType st =
+        st_dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
+    return hip_status(fn, gdr::launch_recurrence(p, s, st, static_cast<hipStream_t>(stream)));
+}
+
+int gdr_fwd_output_shape(const gdr_tensor* qkv_conv_output, const gdr_tensor* recurrent_state,
+                         int64_t out_shape[2]) {
+    const char* fn = "gdr_fwd_output_shape";
+    if (!qkv_conv_output || !recurrent_state || !out_shape)
+        return fail(GDR_ERR_INVALID_ARG, "%s: null argument", fn);
+    if (qkv_conv_output->ndim != 2 || recurrent_state->ndim != 4)
+        return fail(GDR_ERR_INVALID_ARG, "%s: expected qkv rank 2 and state rank 4", fn);
+    out_shape[0] = qkv_conv_output->shape[0];
+    out_shape[1] = recurrent_state->shape[1] * recurrent_state->shape[3];
+    g_last_error.clear();
+    return GDR_OK;
+}
+
+int64_t gdr_ring_record_elements(int32_t group, int32_t key_head_dim, int32_t value_head_dim) {
+    if (group < 1 || key_head_dim < 1 || value_head_dim < 1) return -1;
+    return static_cast<int64_t>(key_head_dim) +
+           static_cast<int64_t>(group) * (static_cast<int64_t>(value_head_dim) + 1);
+}
+
+const char* gdr_last_error_message(void) { return g_last_error.c_str(); }
+
+const char* gdr_version(void) { return "gdr 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal launch parameters shared by the host entry points and the gfx950
+// kernels of the gated delta rule library.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+constexpr uint32_t kPadSlot = 0xFFFFFFFFu;
+
+// One launch of the recurrence kernel.  All strides are in elements.
+// A token tensor X of row r, sequence-local token t and head hd lives at
+//   X + (offsets ? offsets[r] * x_tok : r * x_seq) + t * x_tok + hd * x_head.
+struct RecParams {
+    int32_t rows;        // batch rows (sequences)
+    int32_t nv, nk, G;   // value heads, key heads, value heads per key head
+    int32_t parts;       // workgroups per (row, key head)
+    int32_t dense_len;   // tokens per row when offsets == nullptr
+    const uint32_t* offsets;
+
+    const float* q; int64_t q_seq, q_tok, q_head;
+    const float* k; int64_t k_seq, k_tok, k_head;
+    const float* v; int64_t v_seq, v_tok, v_head;
+    const float* gate; int64_t g_seq, g_tok, g_head;   // nullptr: a = 1
+    int32_t gate_is_log;                               // a = exp(gate)
+    const float* beta; int64_t b_seq, b_tok, b_head;   // nullptr: beta = 1
+    float* out; int64_t o_seq, o_tok, o_head;
+
+    // State: slot = slot_idx[row] (nullptr: slot = row).  kPadSlot pads.
+    const uint32_t* slot_idx;
+    const void* src; int64_t src_slot, src_head; int32_t src_by_slot;  // nullptr: zeros
+    void* dst; int64_t dst_slot, dst_head; int32_t dst_by_slot;        // nullptr: no store
+
+    // Snapshots (fused update): entry i after (i+1)*spt steps, at dst slot.
+    void* snap; int64_t snap_slot, snap_tok, snap_head; int32_t snap_count, spt;
+
+    // Verify ring: rows with length <= ring_len record and do not store.
+    float* ring; const uint32_t* ring_idx;
+    int64_t ring_row, ring_head, ring_tok; int32_t ring_len;
+
+    float scale;
+    int32_t l2norm;
+};
+
+struct FoldParams {
+    int32_t rows, nv, nk, G, parts;
+    const uint32_t* slot_idx;
+    void* state; int64_t st_slot, st_head;
+    const float* ring; const uint32_t* ring_idx;
+    int64_t ring_row, ring_head, ring_tok; int32_t ring_len;
+    const uint32_t* accepted;
+};
+
+enum class StateType { F32 = 0, BF16 = 1 };
+
+// Launch configuration picked by the host for one call.
+struct LaunchShape {
+    int K;          // == V
+    int cpl;        // value columns per lane (8 lanes share one key-row group)
+    int chunk;      // tokens staged per barrier
+    int wpg;        // waves per workgroup
+};
+
+// Host-side launchers (defined next to the kernels).  Return hipError_t.
+hipError_t launch_recurrence(const RecParams& p, const LaunchShape& s, StateType st,
+                             hipStream_t stream);
+hipError_t launch_fold(const FoldParams& p, const LaunchShape& s, StateType st,
+                       hipStream_t stream);
+
+// Columns per wave for a given lanes-per-column setting.
+constexpr int kLanesPerRow = 8;   // lanes that share one key-row group
+constexpr int kRowGroups = 8;     // key-row groups per wave (64 / 8)
+
+}  // namespace gdr

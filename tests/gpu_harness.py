@@ -1,0 +1,155 @@
+"""Helpers of the GPU parity tests: move seeded NumPy inputs to the device,
+call the library through its binding, bring results back, and compare with
+the oracle at the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import gated_delta_rule_loop_amd as gdr
+from gated_delta_rule_loop_amd import workloads as wl
+
+REL_TOL = 2e-3          # max |got - ref| <= REL_TOL * max |ref|
+FLIP_MARGIN = 1e-4      # a bf16 flip is a tie only within this * max|ref| of the midpoint
+FLIP_FRACTION = 1e-3    # at most this fraction of elements may be such ties
+
+
+def dev(a):
+    """NumPy -> device tensor; uint16 is bf16 bits, uint32 goes to int32 bits."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    if t is None:
+        return None
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def gpu_fwd(w, *, scale=None, l2norm=True, out=None):
+    d = {k: dev(w[k]) for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets")}
+    T = w["qkv"].shape[0]
+    V = w["state"].shape[3]
+    if out is None:
+        out = torch.full((T, w["num_value_heads"] * V), float("nan"), device="cuda")
+    sc = w.get("scale") if scale is None else scale
+    gdr.gdr_recurrence_fwd(out, d["state"], d["slot_idx"], d["qkv"], d["decay"], d["beta"],
+                           d["row_offsets"], num_value_heads=w["num_value_heads"],
+                           num_key_heads=w["num_key_heads"], scale=sc, l2norm=l2norm)
+    torch.cuda.synchronize()
+    return host(out), host(d["state"])
+
+
+def gpu_verify(w, *, ring=None, scale=None):
+    d = {k: dev(w[k]) for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets",
+                                "ring_slot_idx")}
+    rg = dev(w["ring"] if ring is None else ring)
+    T = w["qkv"].shape[0]
+    V = w["state"].shape[3]
+    out = torch.full((T, w["num_value_heads"] * V), float("nan"), device="cuda")
+    gdr.gdr_recurrence_verify_ring(out, d["state"], d["slot_idx"], d["qkv"], d["decay"],
+                                   d["beta"], d["row_offsets"], rg, d["ring_slot_idx"],
+                                   num_value_heads=w["num_value_heads"],
+                                   num_key_heads=w["num_key_heads"], scale=scale)
+    torch.cuda.synchronize()
+    return host(out), host(d["state"]), host(rg)
+
+
+def gpu_fold(w, state, ring, accepted):
+    st = dev(state)
+    gdr.gdr_state_fold(st, dev(w["slot_idx"]), dev(ring), dev(w["ring_slot_idx"]),
+                       dev(np.asarray(accepted, np.uint32)), num_value_heads=w["num_value_heads"],
+                       num_key_heads=w["num_key_heads"])
+    torch.cuda.synchronize()
+    return host(st)
+
+
+def gpu_fused(w, **over):
+    args = dict(w)
+    args.update(over)
+    t = {k: dev(args.get(k)) for k in ("q", "k", "v", "g", "beta", "state", "initial_state",
+                                       "intermediate_states", "cu_seqlens")}
+    idx = args.get("state_indices")
+    idx_t = None if idx is None else dev(np.asarray(idx, np.int32))
+    o, fin = gdr.gdr_fused_recurrent_update(
+        t["q"], t["k"], t["v"], g=t["g"], beta=t["beta"], scale=args.get("scale"),
+        initial_state=t["initial_state"], output_final_state=args.get("output_final_state", False),
+        use_qk_l2norm_in_kernel=args.get("use_qk_l2norm_in_kernel", False),
+        cu_seqlens=t["cu_seqlens"], state=t["state"], state_indices=idx_t,
+        intermediate_states=t["intermediate_states"],
+        steps_per_token=args.get("steps_per_token", 1))
+    torch.cuda.synchronize()
+    return host(o), host(fin), host(t["intermediate_states"])
+
+
+# ------------------------------------------------------------ comparisons ---
+
+def as_f32(a):
+    a = np.asarray(a)
+    return wl.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
+
+
+def assert_close(got, ref, what, rel=REL_TOL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    scale = np.abs(ref).max(initial=0.0)
+    err = np.abs(got - ref).max(initial=0.0)
+    assert err <= rel * max(scale, 1e-30), (
+        f"{what}: max err {err:.3e} > {rel:.0e} * max|ref| {scale:.3e}")
+    return err / max(scale, 1e-30)
+
+
+def _bf16_neighbours(x):
+    """The bf16 values just below and above float32 x (truncation and +1 ulp)."""
+    bits = x.astype(np.float32).view(np.uint32)
+    lo = (bits & 0xFFFF0000).view(np.float32)
+    step = (((bits & 0xFFFF0000) + 0x10000).astype(np.uint32)).view(np.float32)
+    return np.minimum(lo, step), np.maximum(lo, step)
+
+
+def assert_state_close(got, ref, what, ref_unrounded=None, rel=REL_TOL):
+    """State parity.  float32 states: plain tolerance.  bf16 states: tolerance
+    against the oracle's bf16 result; an element beyond it is accepted only as
+    a rounding tie - it must be the other bf16 neighbour of the oracle's
+    unrounded float32 value, which must lie within FLIP_MARGIN * max|ref| of
+    the midpoint between the two neighbours - and such ties are capped at
+    FLIP_FRACTION of the elements.  Returns the number of ties."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    g, r = as_f32(got).astype(np.float64), as_f32(ref).astype(np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    scale = max(np.abs(r).max(initial=0.0), 1e-30)
+    bad = np.abs(g - r) > rel * scale
+    if not bad.any():
+        return 0
+    assert got.dtype == np.uint16 and ref_unrounded is not None, (
+        f"{what}: max err {np.abs(g - r).max():.3e} > {rel:.0e} * {scale:.3e}")
+    u = np.asarray(ref_unrounded, np.float32)[bad]
+    lo, hi = _bf16_neighbours(u)
+    gb = g[bad]
+    is_neighbour = (gb == lo) | (gb == hi)
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2
+    near_tie = np.abs(u.astype(np.float64) - mid) <= FLIP_MARGIN * scale
+    ok = is_neighbour & near_tie
+    assert ok.all(), (f"{what}: {int((~ok).sum())} elements beyond tolerance are not bf16 "
+                      f"rounding ties (max err {np.abs(g - r).max():.3e}, scale {scale:.3e})")
+    n = int(bad.sum())
+    assert n <= FLIP_FRACTION * got.size, f"{what}: {n} rounding ties (> {FLIP_FRACTION:.0e})"
+    return n
+
+
+def f32_pool(state):
+    """The same pool values held as float32 (to obtain unrounded oracle states)."""
+    return as_f32(state).copy()
