@@ -1,0 +1,365 @@
+"""Benchmark of the gated delta rule recurrence on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c1,c2,c3,c4]
+                    [--no-cpu-baseline] [--copy-probe MiB]
+
+Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
+bf16 state pool of 512 slots) through gdr_recurrence_fwd; `value` is decode
+tokens/s with every input already resident in HBM.  Cold-cache protocol: R
+independent sets of (pool, inputs, outputs) are rotated so that consecutive
+launches touch disjoint memory (R * 512 MiB of pool, well above the 256 MB
+Infinity Cache).  The per-launch time is the HIP-event time of the timed
+region on the stream the kernels run on, divided by the launch count.
+
+Also timed (reported under "configs"): the ragged prefill (VALU-bound), the
+speculative verify + fold (HBM-bound) and the Gated DeltaProduct decode with
+snapshots (HBM-bound).  The CPU baseline is the plain C oracle timed on the
+host on a bounded sample of the decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz, unpacked
+VALU_FP32_PACKED_TFLOPS = 157.3  # with packed fp32 (not used by these kernels)
+FLOPS_PER_TOKEN_HEAD_ELEM = 7    # decay 1, S^T k 2, rank-1 write 2, S^T q 2 per state element
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gdr_kernels.hip", "gdr_api.cpp", "gdr_internal.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_loop_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(case):
+    """HBM traffic per launch measured with rocprofv3 counters, if the summary
+    in profiles/ was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{case}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^traffic-json: (\{.*\})$", open(path).read(), flags=re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_hash") != kernel_source_hash():
+        return None
+    return d
+
+
+# ------------------------------------------------------------------ cases ---
+
+class Case:
+    """One timed workload: R rotation sets and a launch for each."""
+
+    def __init__(self, name, launches, alg_bytes, state_bytes, tokens, flops=0.0, extra=None):
+        self.name = name
+        self.launches = launches
+        self.alg_bytes = alg_bytes
+        self.state_bytes = state_bytes
+        self.tokens = tokens
+        self.flops = flops
+        self.extra = extra or {}
+
+
+def _dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _packed_launch(torch, gdr, B, w, ring=False, stream=None):
+    """Prebuilt C-ABI call of the forward (or verify) on device copies of w."""
+    d = {k: _dev(torch, w[k]) for k in ("qkv", "decay", "beta", "state", "slot_idx",
+                                       "row_offsets")}
+    T = w["qkv"].shape[0]
+    V = w["state"].shape[3]
+    d["out"] = torch.empty((T, w["num_value_heads"] * V), dtype=torch.float32, device="cuda")
+    keep = dict(d)
+    L = B.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    descs = [B.describe(d[k]) for k in ("out", "state", "slot_idx", "qkv", "decay", "beta",
+                                        "row_offsets")]
+    refs = [ctypes.byref(x) for x in descs]
+    nv, nk = w["num_value_heads"], w["num_key_heads"]
+    if ring:
+        keep["ring"] = _dev(torch, w["ring"])
+        keep["ring_slot_idx"] = _dev(torch, w["ring_slot_idx"])
+        rdesc = [B.describe(keep["ring"]), B.describe(keep["ring_slot_idx"])]
+        refs += [ctypes.byref(x) for x in rdesc]
+        descs += rdesc
+
+        def launch():
+            rc = L.gdr_recurrence_verify_ring(nv, nk, *refs, ctypes.c_float(-1.0), 1, st)
+            assert rc == 0, B.gdr_last_error_message()
+    else:
+        def launch():
+            rc = L.gdr_recurrence_fwd(nv, nk, *refs, ctypes.c_float(-1.0), 1, st)
+            assert rc == 0, B.gdr_last_error_message()
+    launch.keep = (keep, descs, refs)
+    return launch, keep
+
+
+def case_decode(torch, gdr, B, wl, rotations):
+    launches = []
+    for r in range(rotations):
+        w = wl.config1(seed=1001 + 100 * r)
+        launch, _ = _packed_launch(torch, gdr, B, w)
+        launches.append(launch)
+    Bn, nv, K = 256, 32, 128
+    state = Bn * nv * K * K * 2 * 2
+    alg = state + Bn * 8192 * 4 + Bn * nv * K * 4 + 2 * Bn * nv * 4 + (2 * Bn + 1) * 4
+    flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
+    return Case("c1_decode", launches, alg, state, Bn, flops)
+
+
+def case_prefill(torch, gdr, B, wl, rotations):
+    w = wl.config2()
+    launches = []
+    for r in range(rotations):
+        launch, _ = _packed_launch(torch, gdr, B, w)
+        launches.append(launch)
+    T = w["qkv"].shape[0]
+    lens = np.diff(w["row_offsets"].astype(np.int64))
+    nv, K = 32, 128
+    state = 8 * nv * K * K * 2 * 2
+    alg = state + w["qkv"].nbytes + T * nv * K * 4 + 2 * T * nv * 4
+    flops = FLOPS_PER_TOKEN_HEAD_ELEM * T * nv * K * K
+    return Case("c2_prefill", launches, alg, state, T, flops,
+                extra={"max_len": int(lens.max()), "lengths": lens.tolist()})
+
+
+def case_verify_fold(torch, gdr, B, wl, rotations):
+    w = wl.config3()
+    lens = np.diff(w["row_offsets"].astype(np.int64))
+    ring_len = w["ring"].shape[2]
+    verifies, folds = [], []
+    for r in range(rotations):
+        launch, keep = _packed_launch(torch, gdr, B, w, ring=True)
+        verifies.append(launch)
+        acc = _dev(torch, w["accepted"])
+        ds = [B.describe(x) for x in (keep["state"], keep["slot_idx"], keep["ring"],
+                                      keep["ring_slot_idx"], acc)]
+        refs = [ctypes.byref(x) for x in ds]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        L = B.lib()
+
+        def fold(refs=refs, st=st, keepalive=(acc, ds, keep)):
+            rc = L.gdr_state_fold(32, 16, *refs, st)
+            assert rc == 0, B.gdr_last_error_message()
+        folds.append(fold)
+    nv, nk, K, V, G = 32, 16, 128, 128, 2
+    head = K * V * 2
+    rec = K + G * (V + 1)
+    T = int(lens.sum())
+    long_rows = lens > ring_len
+    state_v = 64 * nv * head + int(long_rows.sum()) * nv * head
+    ring_w = int(lens[~long_rows].sum()) * nk * rec * 4
+    alg_v = state_v + ring_w + w["qkv"].nbytes + T * nv * V * 4 + 2 * T * nv * 4
+    acc = w["accepted"].astype(np.int64)
+    fold_rows = (acc > 0) & (acc <= ring_len)
+    state_f = int(fold_rows.sum()) * nv * head * 2
+    alg_f = state_f + int(acc[fold_rows].sum()) * nk * rec * 4
+    cv = Case("c3_verify", verifies, alg_v, state_v + ring_w, T,
+              FLOPS_PER_TOKEN_HEAD_ELEM * T * nv * K * V,
+              extra={"long_rows": int(long_rows.sum())})
+    cf = Case("c3_fold", folds, alg_f, state_f, int(acc[fold_rows].sum()),
+              2 * 2 * int(acc[fold_rows].sum()) * nv * K * V,
+              extra={"folded_rows": int(fold_rows.sum())})
+    return cv, cf
+
+
+def case_gdp(torch, gdr, B, wl, rotations):
+    launches = []
+    w0 = None
+    for r in range(rotations):
+        w = wl.config4(seed=1004 + 100 * r)
+        w0 = w0 or w
+        t = {k: _dev(torch, w[k]) for k in ("q", "k", "v", "g", "beta", "state",
+                                           "intermediate_states")}
+        t["idx"] = _dev(torch, w["state_indices"].astype(np.int32))
+        t["o"] = torch.empty(w["v"].shape, dtype=torch.float32, device="cuda")
+        ds = {k: B.describe(v) for k, v in t.items()}
+        L = B.lib()
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        r_ = ctypes.byref
+        args = (r_(ds["q"]), r_(ds["k"]), r_(ds["v"]), r_(ds["g"]), r_(ds["beta"]),
+                ctypes.c_float(-1.0), None, None, 1, None, r_(ds["state"]), r_(ds["idx"]),
+                r_(ds["intermediate_states"]), 2, r_(ds["o"]), st)
+
+        def launch(args=args, keep=(t, ds)):
+            rc = L.gdr_fused_recurrent_update(*args)
+            assert rc == 0, B.gdr_last_error_message()
+        launches.append(launch)
+    idx = w0["state_indices"]
+    act = int((idx >= 0).sum())
+    HV, H, K, V, T = 32, 16, 128, 128, 8
+    head = K * V * 2
+    state = act * HV * head * 2 + act * HV * head * (T // 2)
+    inputs = act * T * (2 * H * K + HV * V + 2 * HV) * 4
+    outs = 128 * T * HV * V * 4
+    return Case("c4_gdp", launches, state + inputs + outs, state, act * T,
+                FLOPS_PER_TOKEN_HEAD_ELEM * act * T * HV * K * V,
+                extra={"active_rows": act, "draft_tokens": act * T // 2})
+
+
+# ----------------------------------------------------------------- timing ---
+
+def time_case(torch, case, steps, warmup):
+    stream = torch.cuda.current_stream()
+    n = len(case.launches)
+    for i in range(warmup):
+        case.launches[i % n]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        case.launches[i % n]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    return ms / steps, wall
+
+
+def summarize(case, ms_per_launch):
+    s = ms_per_launch * 1e-3
+    d = {"us_per_launch": round(ms_per_launch * 1e3, 2),
+         "tokens_per_s": round(case.tokens / s, 1),
+         "alg_bytes_per_launch": int(case.alg_bytes),
+         "alg_GBps": round(case.alg_bytes / s / 1e9, 1),
+         "state_GBps": round(case.state_bytes / s / 1e9, 1),
+         "hbm_frac": round(case.alg_bytes / s / 1e9 / HBM_PEAK_GBS, 4)}
+    if case.flops:
+        tf = case.flops / s / 1e12
+        d["alg_TFLOPs"] = round(tf, 2)
+        d["valu_frac_unpacked"] = round(tf / VALU_FP32_PEAK_TFLOPS, 4)
+        d["valu_frac_packed_peak"] = round(tf / VALU_FP32_PACKED_TFLOPS, 4)
+    d.update(case.extra)
+    return d
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle as it stands, single-threaded, on whole decode batches."""
+    import oracle
+    w = wl.config1()
+    args = {k: w[k] for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets",
+                              "num_value_heads", "num_key_heads")}
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.recurrence_fwd(**args)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(256 * reps / t_total, 1), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full decode batch (256 sequences x 32 value heads, K=V=128, bf16 "
+                      f"pool), {reps} repetitions, {t_total:.1f} s single-threaded"}
+
+
+def copy_probe(torch, mib):
+    """A plain device copy of known size, for calibrating the HBM counters."""
+    x = torch.empty(mib * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": x.numel(), "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotations", type=int, default=4)
+    ap.add_argument("--only", default="c1,c2,c3,c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: the recurrence has no cross-GPU step in this "
+              "build; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_loop_amd as gdr
+    from gated_delta_rule_loop_amd import _binding as B
+    from gated_delta_rule_loop_amd import workloads as wl
+
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+        return
+    B.lib()
+    only = set(args.only.split(","))
+    cases = []
+    if "c1" in only:
+        cases.append(case_decode(torch, gdr, B, wl, args.rotations))
+    if "c2" in only:
+        cases.append(case_prefill(torch, gdr, B, wl, 2))
+    if "c3" in only:
+        cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations))
+    if "c4" in only:
+        cases.append(case_gdp(torch, gdr, B, wl, 2))
+    torch.cuda.synchronize()
+
+    results = {}
+    head = None
+    for c in cases:
+        steps = args.steps if c.name != "c2_prefill" else max(5, args.steps // 40)
+        ms, wall = time_case(torch, c, steps, args.warmup if c.name != "c2_prefill" else 2)
+        results[c.name] = summarize(c, ms)
+        results[c.name]["launches_timed"] = steps
+        print(f"# {c.name}: {json.dumps(results[c.name])}", file=sys.stderr, flush=True)
+        if c.name == "c1_decode":
+            head = (c, ms, steps)
+
+    line = {"metric": "decode tokens/sec and achieved state HBM GB/s (% peak), 1 MI355X",
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "configs": results}
+    if head is not None:
+        c, ms, steps = head
+        s = ms * 1e-3
+        line.update({"value": round(c.tokens / s, 1), "ms_per_step": round(ms, 5),
+                     "config": {"workload": "decode step: 256 sequences x 1 token, nk=16 key "
+                                            "heads, nv=32 value heads, K=V=128, bf16 state "
+                                            "pool of 512 slots, f32 inputs",
+                                "batch": 256, "tokens_per_sequence": 1,
+                                "state_dtype": "bf16", "cold_cache_rotations": args.rotations},
+                     "state_GBps": results["c1_decode"]["state_GBps"]})
+        tr = read_traffic("c1_decode")
+        line["roofline"] = {"bound": "hbm", "achieved": round(c.alg_bytes / s / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(c.alg_bytes / s / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": None if tr is None else tr["bytes_per_launch"]}
+    else:
+        line.update({"value": None, "ms_per_step": None, "config": {"workload": args.only}})
+    if not args.no_cpu_baseline and "c1" in only:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
