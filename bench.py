@@ -1,6 +1,6 @@
 """Benchmark of the gated delta rule recurrence on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c1,c2,c3,c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,verify,gdp]
                     [--no-cpu-baseline] [--copy-probe MiB]
 
 Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
@@ -49,7 +49,7 @@ def kernel_source_hash():
 def read_traffic(case):
     """HBM traffic per launch measured with rocprofv3 counters, if the summary
     in profiles/ was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{case}.md")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{case}.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"^traffic-json: (\{.*\})$", open(path).read(), flags=re.M)
@@ -120,18 +120,18 @@ def _packed_launch(torch, gdr, B, w, ring=False, stream=None):
 def case_decode(torch, gdr, B, wl, rotations):
     launches = []
     for r in range(rotations):
-        w = wl.config1(seed=1001 + 100 * r)
+        w = wl.decode_step(seed=1001 + 100 * r)
         launch, _ = _packed_launch(torch, gdr, B, w)
         launches.append(launch)
     Bn, nv, K = 256, 32, 128
     state = Bn * nv * K * K * 2 * 2
     alg = state + Bn * 8192 * 4 + Bn * nv * K * 4 + 2 * Bn * nv * 4 + (2 * Bn + 1) * 4
     flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
-    return Case("c1_decode", launches, alg, state, Bn, flops)
+    return Case("decode_256x1", launches, alg, state, Bn, flops)
 
 
 def case_prefill(torch, gdr, B, wl, rotations):
-    w = wl.config2()
+    w = wl.ragged_prefill()
     launches = []
     for r in range(rotations):
         launch, _ = _packed_launch(torch, gdr, B, w)
@@ -142,12 +142,12 @@ def case_prefill(torch, gdr, B, wl, rotations):
     state = 8 * nv * K * K * 2 * 2
     alg = state + w["qkv"].nbytes + T * nv * K * 4 + 2 * T * nv * 4
     flops = FLOPS_PER_TOKEN_HEAD_ELEM * T * nv * K * K
-    return Case("c2_prefill", launches, alg, state, T, flops,
+    return Case("prefill_8x4096", launches, alg, state, T, flops,
                 extra={"max_len": int(lens.max()), "lengths": lens.tolist()})
 
 
 def case_verify_fold(torch, gdr, B, wl, rotations):
-    w = wl.config3()
+    w = wl.verify_window()
     lens = np.diff(w["row_offsets"].astype(np.int64))
     ring_len = w["ring"].shape[2]
     verifies, folds = [], []
@@ -177,10 +177,10 @@ def case_verify_fold(torch, gdr, B, wl, rotations):
     fold_rows = (acc > 0) & (acc <= ring_len)
     state_f = int(fold_rows.sum()) * nv * head * 2
     alg_f = state_f + int(acc[fold_rows].sum()) * nk * rec * 4
-    cv = Case("c3_verify", verifies, alg_v, state_v + ring_w, T,
+    cv = Case("verify_64x12", verifies, alg_v, state_v + ring_w, T,
               FLOPS_PER_TOKEN_HEAD_ELEM * T * nv * K * V,
               extra={"long_rows": int(long_rows.sum())})
-    cf = Case("c3_fold", folds, alg_f, state_f, int(acc[fold_rows].sum()),
+    cf = Case("fold_64x12", folds, alg_f, state_f, int(acc[fold_rows].sum()),
               2 * 2 * int(acc[fold_rows].sum()) * nv * K * V,
               extra={"folded_rows": int(fold_rows.sum())})
     return cv, cf
@@ -190,7 +190,7 @@ def case_gdp(torch, gdr, B, wl, rotations):
     launches = []
     w0 = None
     for r in range(rotations):
-        w = wl.config4(seed=1004 + 100 * r)
+        w = wl.gdp_decode(seed=1004 + 100 * r)
         w0 = w0 or w
         t = {k: _dev(torch, w[k]) for k in ("q", "k", "v", "g", "beta", "state",
                                            "intermediate_states")}
@@ -215,7 +215,7 @@ def case_gdp(torch, gdr, B, wl, rotations):
     state = act * HV * head * 2 + act * HV * head * (T // 2)
     inputs = act * T * (2 * H * K + HV * V + 2 * HV) * 4
     outs = 128 * T * HV * V * 4
-    return Case("c4_gdp", launches, state + inputs + outs, state, act * T,
+    return Case("gdp_128x8", launches, state + inputs + outs, state, act * T,
                 FLOPS_PER_TOKEN_HEAD_ELEM * act * T * HV * K * V,
                 extra={"active_rows": act, "draft_tokens": act * T // 2})
 
@@ -261,7 +261,7 @@ def summarize(case, ms_per_launch):
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle as it stands, single-threaded, on whole decode batches."""
     import oracle
-    w = wl.config1()
+    w = wl.decode_step()
     args = {k: w[k] for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets",
                               "num_value_heads", "num_key_heads")}
     reps, t_total = 0, 0.0
@@ -294,7 +294,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotations", type=int, default=4)
-    ap.add_argument("--only", default="c1,c2,c3,c4")
+    ap.add_argument("--only", default="decode,prefill,verify,gdp")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -314,25 +314,25 @@ def main():
     B.lib()
     only = set(args.only.split(","))
     cases = []
-    if "c1" in only:
+    if "decode" in only:
         cases.append(case_decode(torch, gdr, B, wl, args.rotations))
-    if "c2" in only:
+    if "prefill" in only:
         cases.append(case_prefill(torch, gdr, B, wl, 2))
-    if "c3" in only:
+    if "verify" in only:
         cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations))
-    if "c4" in only:
+    if "gdp" in only:
         cases.append(case_gdp(torch, gdr, B, wl, 2))
     torch.cuda.synchronize()
 
     results = {}
     head = None
     for c in cases:
-        steps = args.steps if c.name != "c2_prefill" else max(5, args.steps // 40)
-        ms, wall = time_case(torch, c, steps, args.warmup if c.name != "c2_prefill" else 2)
+        steps = args.steps if c.name != "prefill_8x4096" else max(5, args.steps // 40)
+        ms, wall = time_case(torch, c, steps, args.warmup if c.name != "prefill_8x4096" else 2)
         results[c.name] = summarize(c, ms)
         results[c.name]["launches_timed"] = steps
         print(f"# {c.name}: {json.dumps(results[c.name])}", file=sys.stderr, flush=True)
-        if c.name == "c1_decode":
+        if c.name == "decode_256x1":
             head = (c, ms, steps)
 
     line = {"metric": "decode tokens/sec and achieved state HBM GB/s (% peak), 1 MI355X",
@@ -348,15 +348,15 @@ def main():
                                             "pool of 512 slots, f32 inputs",
                                 "batch": 256, "tokens_per_sequence": 1,
                                 "state_dtype": "bf16", "cold_cache_rotations": args.rotations},
-                     "state_GBps": results["c1_decode"]["state_GBps"]})
-        tr = read_traffic("c1_decode")
+                     "state_GBps": results["decode_256x1"]["state_GBps"]})
+        tr = read_traffic("rec_kernel_decode_256x1tok")
         line["roofline"] = {"bound": "hbm", "achieved": round(c.alg_bytes / s / 1e9, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(c.alg_bytes / s / 1e9 / HBM_PEAK_GBS, 4),
                             "traffic": None if tr is None else tr["bytes_per_launch"]}
     else:
         line.update({"value": None, "ms_per_step": None, "config": {"workload": args.only}})
-    if not args.no_cpu_baseline and "c1" in only:
+    if not args.no_cpu_baseline and "decode" in only:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
 

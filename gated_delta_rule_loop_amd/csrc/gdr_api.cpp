@@ -105,19 +105,41 @@ float resolve_scale(float scale, int64_t K) {
     return scale;
 }
 
-// Launch shape: few tokens per row -> wide column tiles (16-byte bf16 state
-// loads, one token per stage); long rows -> narrow tiles (more waves for the
-// token-serial chain) and 16-token stages.  The reduction order does not
-// depend on this choice.
-gdr::LaunchShape pick_shape(int64_t K, int64_t G, int64_t total_tokens, int64_t rows) {
+// Launch shape, by entry and row length: about one token per row -> decode
+// tiles (one token per stage, high occupancy); short windows -> wider stages;
+// the fused update on short rows (snapshot stores dominate) -> 16-byte state
+// accesses; long rows (>= 16 tokens per row on average) -> narrow tiles, so
+// the token-serial chain is spread over more waves.  The reduction order does
+// not depend on this choice.
+enum class Entry { Packed, Fused, Fold };
+
+gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t G, int64_t total_tokens, int64_t rows) {
     gdr::LaunchShape s{};
     s.K = static_cast<int>(K);
     const bool long_rows = rows > 0 && total_tokens >= 16 * rows;
-    if (long_rows) {
+    const bool decode = rows > 0 && 2 * total_tokens <= 3 * rows;  // ~1 token per row
+    if (K == 128) {
+        if (e == Entry::Fold) {
+            s.cpl = GDR_FOLD_CPL;
+            s.chunk = 1;
+        } else if (long_rows) {
+            s.cpl = GDR_LONG_CPL;
+            s.chunk = GDR_LONG_CHUNK;
+        } else if (e == Entry::Fused && !decode) {
+            s.cpl = GDR_FUSED_CPL;
+            s.chunk = GDR_FUSED_CHUNK;
+        } else if (decode) {
+            s.cpl = GDR_DECODE_CPL;
+            s.chunk = GDR_DECODE_CHUNK;
+        } else {
+            s.cpl = GDR_SHORT_CPL;
+            s.chunk = GDR_SHORT_CHUNK;
+        }
+    } else if (long_rows && e != Entry::Fold) {
         s.cpl = 2;
         s.chunk = 16;
     } else {
-        s.cpl = K == 128 ? 4 : (K == 64 ? 8 : (K == 32 ? 4 : 2));
+        s.cpl = K == 64 ? 8 : (K == 32 ? 4 : 2);
         s.chunk = 8;
     }
     const int64_t tiles = K / (gdr::kLanesPerRow * s.cpl);
@@ -204,7 +226,7 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     if (B * nk > (int64_t{1} << 28))
         return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
 
-    const gdr::LaunchShape s = pick_shape(K, G, T, B);
+    const gdr::LaunchShape s = pick_shape(Entry::Packed, K, G, T, B);
     const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
     p.rows = static_cast<int32_t>(B);
     p.nv = nv;
@@ -311,7 +333,7 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
         g_last_error.clear();
         return GDR_OK;
     }
-    gdr::LaunchShape s = pick_shape(K, G, B, B);  // wide tiles
+    gdr::LaunchShape s = pick_shape(Entry::Fold, K, G, B, B);
     const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
     gdr::FoldParams p{};
     p.rows = static_cast<int32_t>(B);
@@ -440,7 +462,7 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     if (N * H > (int64_t{1} << 28)) return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
 
     const int64_t G = HV / H;
-    const gdr::LaunchShape s = pick_shape(K, G, B * T, N);
+    const gdr::LaunchShape s = pick_shape(Entry::Fused, K, G, B * T, N);
     const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
     p.rows = static_cast<int32_t>(N);
     p.nv = static_cast<int32_t>(HV);

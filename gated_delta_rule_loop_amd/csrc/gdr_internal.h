@@ -68,6 +68,38 @@ hipError_t launch_recurrence(const RecParams& p, const LaunchShape& s, StateType
 hipError_t launch_fold(const FoldParams& p, const LaunchShape& s, StateType st,
                        hipStream_t stream);
 
+// Launch profiles at K = 128 (value columns per lane, tokens per stage).  The
+// reduction order does not depend on them, so they are free tuning choices:
+// decode (about one token per row), short windows (verify), the fused update
+// on short rows (GDP decode, snapshot-heavy), and long rows (prefill).
+#ifndef GDR_DECODE_CPL
+#define GDR_DECODE_CPL 4
+#endif
+#ifndef GDR_DECODE_CHUNK
+#define GDR_DECODE_CHUNK 1
+#endif
+#ifndef GDR_SHORT_CPL
+#define GDR_SHORT_CPL 4
+#endif
+#ifndef GDR_SHORT_CHUNK
+#define GDR_SHORT_CHUNK 8
+#endif
+#ifndef GDR_FUSED_CPL
+#define GDR_FUSED_CPL 8
+#endif
+#ifndef GDR_FUSED_CHUNK
+#define GDR_FUSED_CHUNK 4
+#endif
+#ifndef GDR_LONG_CPL
+#define GDR_LONG_CPL 1
+#endif
+#ifndef GDR_LONG_CHUNK
+#define GDR_LONG_CHUNK 16
+#endif
+#ifndef GDR_FOLD_CPL
+#define GDR_FOLD_CPL 4
+#endif
+
 // Columns per wave for a given lanes-per-column setting.
 constexpr int kLanesPerRow = 8;   // lanes that share one key-row group
 constexpr int kRowGroups = 8;     // key-row groups per wave (64 / 8)

@@ -148,6 +148,25 @@ __device__ __forceinline__ void store_cols(float* p, const float* s) {
 
 // ---------------------------------------------------- per-lane arithmetic ---
 
+// The state of one (row, value head) is held as scale * S: a token's decay
+// multiplies only the scalar (cn = scale * a), and the rank-1 write becomes
+// S += k_hat (u / cn)^T, one fused multiply-add per element.  When cn leaves
+// [2^-64, 2^64] (a zero decay included) the scale is folded into the registers
+// and reset to 1.  The forward, the verify and the fold run this same scalar
+// sequence from the same decays, so their states stay bit-identical.
+constexpr float kScaleLo = 5.421010862427522e-20f;  // 2^-64
+constexpr float kScaleHi = 1.8446744073709552e19f;  // 2^64
+
+template <int R, int CPL>
+__device__ __forceinline__ float decay_step(float (&S)[R][CPL], float cn) {
+    if (cn >= kScaleLo && cn <= kScaleHi) return cn;
+#pragma unroll
+    for (int ri = 0; ri < R; ++ri)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) S[ri][cc] = cn * S[ri][cc];
+    return 1.0f;
+}
+
 // out[c] = sum_ri S[ri][c] * vec[ri], ascending ri, fused multiply-adds.
 template <int R, int CPL>
 __device__ __forceinline__ void dot_rows(const float (&S)[R][CPL], const float (&vec)[R],
@@ -183,107 +202,140 @@ __device__ __forceinline__ int pad_index(int i) { return i + (i / R) * 4; }
 
 // ------------------------------------------------------------- recurrence ---
 
+// One work item: value columns [j0, j0 + CPL) of every key row, for one value
+// head of one row, resolved once per item.
+struct Item {
+    int row, h, part, m, vt, hv, j0, L;
+    int64_t rq, rk, rv, rg, rb, ro;
+    uint32_t slot;
+    bool pad, record;
+};
+
 template <int K, int CPL, int C, int WPG, typename ST>
-__global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
-    constexpr int V = K;
-    constexpr int R = K / kRowGroups;
-    constexpr int BV = kLanesPerRow * CPL;
-    constexpr int TILES = V / BV;
-    constexpr int KP = K + 4 * kRowGroups;       // padded staged vector
-    constexpr int QK = (K + 63) / 64;            // q/k elements per lane (norm)
-    constexpr int SPW = (C + WPG - 1) / WPG;     // tokens normalised per wave
-    constexpr int VTOT = C * BV;                 // v floats per wave per chunk
-    constexpr int VPL = VTOT >= 64 ? VTOT / 64 : 1;
+struct Rec {
+    static constexpr int V = K;
+    static constexpr int R = K / kRowGroups;
+    static constexpr int BV = kLanesPerRow * CPL;
+    static constexpr int TILES = V / BV;
+    static constexpr int KP = K + 4 * kRowGroups;      // padded staged vector
+    static constexpr int QK = (K + 63) / 64;           // q/k elements per lane (norm)
+    static constexpr int SPW = (C + WPG - 1) / WPG;    // tokens normalised per wave
+    static constexpr int VTOT = C * BV;                // v floats per wave per chunk
+    static constexpr int VPL = VTOT >= 64 ? VTOT / 64 : 1;
     static_assert(R >= 2 && TILES >= 1 && V % BV == 0, "tile shape");
     static_assert(VTOT < 64 || VTOT % 64 == 0, "v staging");
     static_assert(C <= 64, "gate staging uses one lane per token");
 
-    constexpr int OFF_K = 0;
-    constexpr int OFF_Q = C * KP;
-    constexpr int OFF_V = 2 * C * KP;
-    constexpr int OFF_A = OFF_V + WPG * VTOT;
-    constexpr int OFF_B = OFF_A + WPG * C;
-    constexpr int BUF = (OFF_B + WPG * C + 3) / 4 * 4;
-    __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
+    // LDS: two chunk buffers of [k_hat C x KP | q_hat*scale C x KP | v | a | beta].
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = C * KP;
+    static constexpr int OFF_V = 2 * C * KP;
+    static constexpr int OFF_A = OFF_V + WPG * VTOT;
+    static constexpr int OFF_B = OFF_A + WPG * C;
+    static constexpr int BUF = (OFF_B + WPG * C + 3) / 4 * 4;
 
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int kg = lane >> 3;
-    const int vl = lane & 7;
+    struct Stage {
+        float q[SPW][QK], k[SPW][QK], v[VPL], a, b;
+    };
 
-    int blk = blockIdx.x;
-    const int part = blk % p.parts;
-    blk /= p.parts;
-    const int h = blk % p.nk;
-    const int row = blk / p.nk;
-    const int unit = part * WPG + w;
-    const int m = unit / TILES;
-    const int vt = unit - m * TILES;
-    const int hv = h * p.G + m;
-    const int j0 = vt * BV + vl * CPL;
-
-    int L;
-    int64_t rq, rk, rv, rg, rb, ro;
-    if (p.offsets) {
-        const int64_t t0 = p.offsets[row];
-        L = static_cast<int>(static_cast<int64_t>(p.offsets[row + 1]) - t0);
-        rq = t0 * p.q_tok; rk = t0 * p.k_tok; rv = t0 * p.v_tok;
-        rg = t0 * p.g_tok; rb = t0 * p.b_tok; ro = t0 * p.o_tok;
-    } else {
-        L = p.dense_len;
-        rq = row * p.q_seq; rk = row * p.k_seq; rv = row * p.v_seq;
-        rg = row * p.g_seq; rb = row * p.b_seq; ro = row * p.o_seq;
-    }
-    const uint32_t slot = p.slot_idx ? p.slot_idx[row] : static_cast<uint32_t>(row);
-    float* outp = p.out + ro + static_cast<int64_t>(hv) * p.o_head + j0;
-
-    if (p.slot_idx && slot == kPadSlot) {  // padding request: zero output only
-        if (kg == 0) {
-            float z[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) z[c] = 0.0f;
-            for (int t = 0; t < L; ++t) store_cols<CPL>(outp + t * p.o_tok, z);
+    __device__ static Item item(const RecParams& p, int idx, int w, int lane) {
+        Item it;
+        int blk = idx;
+        it.part = blk % p.parts;
+        blk /= p.parts;
+        it.h = blk % p.nk;
+        it.row = blk / p.nk;
+        const int unit = it.part * WPG + w;
+        it.m = unit / TILES;
+        it.vt = unit - it.m * TILES;
+        it.hv = it.h * p.G + it.m;
+        it.j0 = it.vt * BV + (lane & 7) * CPL;
+        if (p.offsets) {
+            const int64_t t0 = p.offsets[it.row];
+            it.L = static_cast<int>(static_cast<int64_t>(p.offsets[it.row + 1]) - t0);
+            it.rq = t0 * p.q_tok; it.rk = t0 * p.k_tok; it.rv = t0 * p.v_tok;
+            it.rg = t0 * p.g_tok; it.rb = t0 * p.b_tok; it.ro = t0 * p.o_tok;
+        } else {
+            const int64_t r = it.row;
+            it.L = p.dense_len;
+            it.rq = r * p.q_seq; it.rk = r * p.k_seq; it.rv = r * p.v_seq;
+            it.rg = r * p.g_seq; it.rb = r * p.b_seq; it.ro = r * p.o_seq;
         }
-        return;
-    }
-    if (L <= 0) return;
-
-    // ---- state tile into registers (issued first: the longest latency) ----
-    float S[R][CPL];
-    const int64_t src_sel = p.src_by_slot ? static_cast<int64_t>(slot) : row;
-    if (p.src) {
-        const ST* sp = static_cast<const ST*>(p.src) + src_sel * p.src_slot +
-                       static_cast<int64_t>(hv) * p.src_head + j0;
-#pragma unroll
-        for (int ri = 0; ri < R; ++ri) load_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
-    } else {
-#pragma unroll
-        for (int ri = 0; ri < R; ++ri)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) S[ri][c] = 0.0f;
+        it.slot = p.slot_idx ? p.slot_idx[it.row] : static_cast<uint32_t>(it.row);
+        it.pad = p.slot_idx != nullptr && it.slot == kPadSlot;
+        it.record = p.ring != nullptr && it.L <= p.ring_len;
+        return it;
     }
 
-    const bool record = p.ring != nullptr && L <= p.ring_len;
-    float* rec = record ? p.ring + static_cast<int64_t>(p.ring_idx[row]) * p.ring_row +
-                              static_cast<int64_t>(h) * p.ring_head
-                        : nullptr;
+    __device__ static float* out_ptr(const RecParams& p, const Item& it) {
+        return p.out + it.ro + static_cast<int64_t>(it.hv) * p.o_head + it.j0;
+    }
 
-    // ---- chunk staging: global -> registers -> (norms) -> LDS ----
-    float sq[SPW][QK], sk[SPW][QK], sv[VPL], sa, sb;
+    __device__ static const ST* src_ptr(const RecParams& p, const Item& it) {
+        const int64_t sel = p.src_by_slot ? static_cast<int64_t>(it.slot) : it.row;
+        return static_cast<const ST*>(p.src) + sel * p.src_slot +
+               static_cast<int64_t>(it.hv) * p.src_head + it.j0;
+    }
 
-    auto load_stage = [&](int c) {
+    // Padding request: +0.0 output for every token, nothing else.
+    __device__ static void zero_output(const RecParams& p, const Item& it, int lane) {
+        if ((lane >> 3) != 0) return;
+        float z[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) z[c] = 0.0f;
+        float* outp = out_ptr(p, it);
+        for (int t = 0; t < it.L; ++t) store_cols<CPL>(outp + t * p.o_tok, z);
+    }
+
+    __device__ static void load_state(const RecParams& p, const Item& it, int kg,
+                                      float (&S)[R][CPL]) {
+        if (p.src) {
+            const ST* sp = src_ptr(p, it);
+#pragma unroll
+            for (int ri = 0; ri < R; ++ri) load_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
+        } else {
+#pragma unroll
+            for (int ri = 0; ri < R; ++ri)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) S[ri][c] = 0.0f;
+        }
+    }
+
+    // Stores the state scale * S.
+    __device__ static void store_tile(ST* base, int kg, float scale, const float (&S)[R][CPL]) {
+#pragma unroll
+        for (int ri = 0; ri < R; ++ri) {
+            float row[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) row[cc] = scale * S[ri][cc];
+            store_cols<CPL>(base + (kg * R + ri) * V, row);
+        }
+    }
+
+    __device__ static void store_state(const RecParams& p, const Item& it, int kg, float scale,
+                                       const float (&S)[R][CPL]) {
+        if (!p.dst || it.record) return;
+        const int64_t sel = p.dst_by_slot ? static_cast<int64_t>(it.slot) : it.row;
+        store_tile(static_cast<ST*>(p.dst) + sel * p.dst_slot +
+                       static_cast<int64_t>(it.hv) * p.dst_head + it.j0,
+                   kg, scale, S);
+    }
+
+    // Global loads of chunk c of an item into registers.
+    __device__ static void load_stage(const RecParams& p, const Item& it, int c, Stage& s,
+                                      int w, int lane) {
         const int tc = c * C;
 #pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int tau = w + s * WPG;
+        for (int i = 0; i < SPW; ++i) {
+            const int tau = w + i * WPG;
             const int t = tc + tau;
-            const bool ok = tau < C && t < L;
+            const bool ok = tau < C && t < it.L;
 #pragma unroll
             for (int e = 0; e < QK; ++e) {
                 const int idx = lane + 64 * e;
                 const bool in = ok && idx < K;
-                sq[s][e] = in ? p.q[rq + t * p.q_tok + h * p.q_head + idx] : 0.0f;
-                sk[s][e] = in ? p.k[rk + t * p.k_tok + h * p.k_head + idx] : 0.0f;
+                s.q[i][e] = in ? p.q[it.rq + t * p.q_tok + it.h * p.q_head + idx] : 0.0f;
+                s.k[i][e] = in ? p.k[it.rk + t * p.k_tok + it.h * p.k_head + idx] : 0.0f;
             }
         }
         {
@@ -291,60 +343,66 @@ __global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
             const int tau = flat / BV;
             const int col = flat - tau * BV;
             const int t = tc + tau;
-            const bool ok = flat < VTOT && t < L;
-            const float* vp = p.v + rv + t * p.v_tok + hv * p.v_head + vt * BV + col;
+            const bool ok = flat < VTOT && t < it.L;
+            const float* vp = p.v + it.rv + t * p.v_tok + it.hv * p.v_head + it.vt * BV + col;
             if constexpr (VPL == 4) {
                 float4 x = ok ? *reinterpret_cast<const float4*>(vp) : make_float4(0, 0, 0, 0);
-                sv[0] = x.x; sv[1] = x.y; sv[2] = x.z; sv[3] = x.w;
+                s.v[0] = x.x; s.v[1] = x.y; s.v[2] = x.z; s.v[3] = x.w;
             } else if constexpr (VPL == 2) {
                 float2 x = ok ? *reinterpret_cast<const float2*>(vp) : make_float2(0, 0);
-                sv[0] = x.x; sv[1] = x.y;
+                s.v[0] = x.x; s.v[1] = x.y;
             } else {
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) sv[i] = ok ? vp[i] : 0.0f;
+                for (int i = 0; i < VPL; ++i) s.v[i] = ok ? vp[i] : 0.0f;
             }
         }
         {
             const int t = tc + lane;
-            const bool ok = lane < C && t < L;
-            sa = 1.0f;
-            sb = 1.0f;
+            const bool ok = lane < C && t < it.L;
+            s.a = 1.0f;
+            s.b = 1.0f;
             if (ok && p.gate) {
-                const float g = p.gate[rg + t * p.g_tok + hv * p.g_head];
-                sa = p.gate_is_log ? expf(g) : g;
+                const float g = p.gate[it.rg + t * p.g_tok + it.hv * p.g_head];
+                s.a = p.gate_is_log ? expf(g) : g;
             }
-            if (ok && p.beta) sb = p.beta[rb + t * p.b_tok + hv * p.b_head];
+            if (ok && p.beta) s.b = p.beta[it.rb + t * p.b_tok + it.hv * p.b_head];
         }
-    };
+    }
 
-    auto commit_stage = [&](int c, float* B) {
+    // Norms of the staged tokens, then k_hat, q_hat*scale, v and gates to LDS.
+    // The first part of a (row, key head) also writes k_hat to the ring.
+    __device__ static void commit_stage(const RecParams& p, const Item& it, int c,
+                                        const Stage& s, float* B, int w, int lane) {
         const int tc = c * C;
+        float* rec = it.record ? p.ring + static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
+                                     static_cast<int64_t>(it.h) * p.ring_head
+                               : nullptr;
 #pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int tau = w + s * WPG;
+        for (int i = 0; i < SPW; ++i) {
+            const int tau = w + i * WPG;
             if (tau >= C) break;
             float rk = 1.0f, rqs = p.scale;
             if (p.l2norm) {
-                float kk = sk[s][0] * sk[s][0];
-                float qq = sq[s][0] * sq[s][0];
+                float kk = s.k[i][0] * s.k[i][0];
+                float qq = s.q[i][0] * s.q[i][0];
 #pragma unroll
                 for (int e = 1; e < QK; ++e) {
-                    kk = __builtin_fmaf(sk[s][e], sk[s][e], kk);
-                    qq = __builtin_fmaf(sq[s][e], sq[s][e], qq);
+                    kk = __builtin_fmaf(s.k[i][e], s.k[i][e], kk);
+                    qq = __builtin_fmaf(s.q[i][e], s.q[i][e], qq);
                 }
                 kk = sum_wave(kk);
                 qq = sum_wave(qq);
                 rk = rsqrtf(kk + kEps);
                 rqs = rsqrtf(qq + kEps) * p.scale;
             }
-            const bool rec_k = record && part == 0 && tc + tau < L;
+            const bool rec_k = it.record && it.part == 0 && tc + tau < it.L;
 #pragma unroll
             for (int e = 0; e < QK; ++e) {
                 const int idx = lane + 64 * e;
                 if (idx < K) {
-                    const float kh = sk[s][e] * rk;
+                    const float kh = s.k[i][e] * rk;
                     B[OFF_K + tau * KP + pad_index<R>(idx)] = kh;
-                    B[OFF_Q + tau * KP + pad_index<R>(idx)] = sq[s][e] * rqs;
+                    B[OFF_Q + tau * KP + pad_index<R>(idx)] = s.q[i][e] * rqs;
                     if (rec_k) rec[(tc + tau) * p.ring_tok + idx] = kh;
                 }
             }
@@ -352,28 +410,29 @@ __global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int flat = lane * VPL + i;
-            if (flat < VTOT) B[OFF_V + w * VTOT + flat] = sv[i];
+            if (flat < VTOT) B[OFF_V + w * VTOT + flat] = s.v[i];
         }
         if (lane < C) {
-            B[OFF_A + w * C + lane] = sa;
-            B[OFF_B + w * C + lane] = sb;
+            B[OFF_A + w * C + lane] = s.a;
+            B[OFF_B + w * C + lane] = s.b;
         }
-    };
+    }
 
-    load_stage(0);
-    commit_stage(0, lds);
-    __syncthreads();
-
-    const int nch = (L + C - 1) / C;
-    for (int c = 0; c < nch; ++c) {
-        const float* B = lds + (c & 1) * BUF;
+    // The tokens of chunk c, staged in B.  The state before the chunk is
+    // scale * S; both are updated (see decay_step for the representation).
+    __device__ static void run_chunk(const RecParams& p, const Item& it, int c, const float* B,
+                                     float (&S)[R][CPL], float& scale, int w, int lane) {
+        const int kg = lane >> 3;
         const int tc = c * C;
-        const int Lc = min(C, L - tc);
-        if (c + 1 < nch) load_stage(c + 1);
+        const int Lc = min(C, it.L - tc);
+        float* outp = out_ptr(p, it);
+        float* rec = it.record ? p.ring + static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
+                                     static_cast<int64_t>(it.h) * p.ring_head
+                               : nullptr;
 
         float kr[R];
         read_rows<R>(B + OFF_K, kg, kr);
-        float x[CPL];
+        float x[CPL];  // S^T k_hat of the next token, before the scale
         dot_rows<R, CPL>(S, kr, x);
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups(x[cc]);
@@ -383,15 +442,21 @@ __global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
             const float be = B[OFF_B + w * C + tau];
             float vv[CPL];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) vv[cc] = B[OFF_V + w * VTOT + tau * BV + vl * CPL + cc];
+            for (int cc = 0; cc < CPL; ++cc)
+                vv[cc] = B[OFF_V + w * VTOT + tau * BV + (lane & 7) * CPL + cc];
+            // r = S_{t-1}^T k_hat with the decay of this token: (scale * a) * x
+            const float cn = scale * a;
             float u[CPL];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) u[cc] = be * (vv[cc] - a * x[cc]);
+            for (int cc = 0; cc < CPL; ++cc) u[cc] = be * (vv[cc] - cn * x[cc]);
+            scale = decay_step<R, CPL>(S, cn);
+            const float rho = __builtin_amdgcn_rcpf(scale);
 #pragma unroll
-            for (int ri = 0; ri < R; ++ri)
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float us = u[cc] * rho;
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc)
-                    S[ri][cc] = __builtin_fmaf(kr[ri], u[cc], a * S[ri][cc]);
+                for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us, S[ri][cc]);
+            }
 
             float qr[R];
             read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
@@ -405,39 +470,66 @@ __global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
                 for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups(x[cc]);
             }
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) o[cc] = sum_row_groups(o[cc]);
+            for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups(o[cc]);
 
             const int t = tc + tau;
             if (kg == 0) store_cols<CPL>(outp + t * p.o_tok, o);
-            if (record) {
+            if (it.record) {
                 float* r = rec + t * p.ring_tok;
-                if (kg == 0) store_cols<CPL>(r + K + m * V + j0, u);
-                if (vt == 0 && lane == 0) r[K + p.G * V + m] = a;
+                if (kg == 0) store_cols<CPL>(r + K + it.m * V + it.j0, u);
+                if (it.vt == 0 && lane == 0) r[K + p.G * V + it.m] = a;
             }
             if (p.snap && (t + 1) % p.spt == 0) {
                 const int i = (t + 1) / p.spt - 1;
-                if (i < p.snap_count) {
-                    ST* sp = static_cast<ST*>(p.snap) + static_cast<int64_t>(slot) * p.snap_slot +
-                             static_cast<int64_t>(i) * p.snap_tok +
-                             static_cast<int64_t>(hv) * p.snap_head + j0;
-#pragma unroll
-                    for (int ri = 0; ri < R; ++ri) store_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
-                }
+                if (i < p.snap_count)
+                    store_tile(static_cast<ST*>(p.snap) + static_cast<int64_t>(it.slot) * p.snap_slot +
+                                   static_cast<int64_t>(i) * p.snap_tok +
+                                   static_cast<int64_t>(it.hv) * p.snap_head + it.j0,
+                               kg, scale, S);
             }
-        }
-        if (c + 1 < nch) {
-            commit_stage(c + 1, lds + ((c + 1) & 1) * BUF);
-            __syncthreads();
         }
     }
 
-    if (p.dst && !record) {
-        const int64_t dsel = p.dst_by_slot ? static_cast<int64_t>(slot) : row;
-        ST* dp = static_cast<ST*>(p.dst) + dsel * p.dst_slot +
-                 static_cast<int64_t>(hv) * p.dst_head + j0;
-#pragma unroll
-        for (int ri = 0; ri < R; ++ri) store_cols<CPL>(dp + (kg * R + ri) * V, S[ri]);
+    // All chunks of an item whose state is scale * S and whose chunk-0 inputs
+    // are in st.
+    __device__ static void run_item(const RecParams& p, const Item& it, float (&S)[R][CPL],
+                                    float& scale, Stage& st, float* lds, int w, int lane) {
+        commit_stage(p, it, 0, st, lds, w, lane);
+        __syncthreads();
+        const int nch = (it.L + C - 1) / C;
+        for (int c = 0; c < nch; ++c) {
+            const bool next = c + 1 < nch;
+            if (next) load_stage(p, it, c + 1, st, w, lane);
+            run_chunk(p, it, c, lds + (c & 1) * BUF, S, scale, w, lane);
+            if (next) {
+                commit_stage(p, it, c + 1, st, lds + ((c + 1) & 1) * BUF, w, lane);
+                __syncthreads();
+            }
+        }
     }
+};
+
+// One work item per workgroup.
+template <int K, int CPL, int C, int WPG, typename ST>
+__global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
+    using Q = Rec<K, CPL, C, WPG, ST>;
+    __shared__ __attribute__((aligned(16))) float lds[2 * Q::BUF];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int kg = lane >> 3;
+    const Item it = Q::item(p, blockIdx.x, w, lane);
+    if (it.pad) {
+        Q::zero_output(p, it, lane);
+        return;
+    }
+    if (it.L <= 0) return;
+    float S[Q::R][CPL];
+    Q::load_state(p, it, kg, S);
+    float scale = 1.0f;
+    typename Q::Stage st;
+    Q::load_stage(p, it, 0, st, w, lane);
+    Q::run_item(p, it, S, scale, st, lds, w, lane);
+    Q::store_state(p, it, kg, scale, S);
 }
 
 // ------------------------------------------------------------------- fold ---
@@ -450,7 +542,7 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
     constexpr int TILES = V / BV;
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int kg = lane >> 3;
     const int vl = lane & 7;
     int blk = blockIdx.x;
@@ -476,6 +568,7 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
 
     const float* rec = p.ring + static_cast<int64_t>(p.ring_idx[row]) * p.ring_row +
                        static_cast<int64_t>(h) * p.ring_head;
+    float scale = 1.0f;
     for (uint32_t t = 0; t < n; ++t) {
         const float* r = rec + static_cast<int64_t>(t) * p.ring_tok;
         const float a = r[K + p.G * V + m];
@@ -492,14 +585,22 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
         }
         float u[CPL];
         load_cols<CPL>(r + K + m * V + j0, u);
+        scale = decay_step<R, CPL>(S, scale * a);
+        const float rho = __builtin_amdgcn_rcpf(scale);
 #pragma unroll
-        for (int ri = 0; ri < R; ++ri)
+        for (int cc = 0; cc < CPL; ++cc) {
+            const float us = u[cc] * rho;
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc)
-                S[ri][cc] = __builtin_fmaf(kr[ri], u[cc], a * S[ri][cc]);
+            for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us, S[ri][cc]);
+        }
     }
 #pragma unroll
-    for (int ri = 0; ri < R; ++ri) store_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
+    for (int ri = 0; ri < R; ++ri) {
+        float row[CPL];
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) row[cc] = scale * S[ri][cc];
+        store_cols<CPL>(sp + (kg * R + ri) * V, row);
+    }
 }
 
 }  // namespace
@@ -523,14 +624,18 @@ static hipError_t launch_rec_st(const RecParams& p, const LaunchShape& s, hipStr
 #define GDR_REC_CASE(KK, CC, CH)                                   \
     if (s.K == KK && s.cpl == CC && s.chunk == CH)                 \
         return launch_rec_wpg<KK, CC, CH, ST>(p, s.wpg, stream);
-    GDR_REC_CASE(128, 4, 8)
-    GDR_REC_CASE(128, 2, 16)
+    GDR_REC_CASE(128, GDR_DECODE_CPL, GDR_DECODE_CHUNK)
+    GDR_REC_CASE(128, GDR_SHORT_CPL, GDR_SHORT_CHUNK)
+    GDR_REC_CASE(128, GDR_FUSED_CPL, GDR_FUSED_CHUNK)
+    GDR_REC_CASE(128, GDR_LONG_CPL, GDR_LONG_CHUNK)
+#ifndef GDR_ONLY_K128
     GDR_REC_CASE(64, 8, 8)
     GDR_REC_CASE(64, 2, 16)
     GDR_REC_CASE(32, 4, 8)
     GDR_REC_CASE(32, 2, 16)
     GDR_REC_CASE(16, 2, 8)
     GDR_REC_CASE(16, 2, 16)
+#endif
 #undef GDR_REC_CASE
     return hipErrorInvalidValue;
 }
@@ -556,10 +661,12 @@ static hipError_t launch_fold_wpg(const FoldParams& p, int wpg, hipStream_t stre
 template <typename ST>
 static hipError_t launch_fold_st(const FoldParams& p, const LaunchShape& s, hipStream_t stream) {
     switch (s.K) {
-        case 128: return s.cpl == 4 ? launch_fold_wpg<128, 4, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
+        case 128: return s.cpl == GDR_FOLD_CPL ? launch_fold_wpg<128, GDR_FOLD_CPL, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
+#ifndef GDR_ONLY_K128
         case 64: return s.cpl == 8 ? launch_fold_wpg<64, 8, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 32: return s.cpl == 4 ? launch_fold_wpg<32, 4, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 16: return s.cpl == 2 ? launch_fold_wpg<16, 2, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
+#endif
         default: return hipErrorInvalidValue;
     }
 }

@@ -15,8 +15,8 @@ Workload shapes follow the operations' documented layouts:
     [S, HV, K, V], state_indices [B] (-1 = padding), intermediate_states
     [S, T // steps_per_token, HV, K, V].
 
-Recipes (one NumPy PCG64 generator per workload, seed = 1000 + config number
-unless given; normals drawn in float64, then cast):
+Recipes (one NumPy PCG64 generator per workload with a fixed default seed;
+normals drawn in float64, then cast):
   q, k, v ~ N(0, 1); decay a = exp(-softplus(z)); beta = sigmoid(z');
   log decay g = -softplus(z); state ~ N(0, sigma) then rounded to the pool
   dtype; slots are distinct random subsets of the pool.
@@ -75,7 +75,7 @@ def packed_inputs(rng, lengths, nk, nv, K, V, slots, state_dtype, state_sigma,
                 row_offsets=offsets, num_value_heads=nv, num_key_heads=nk)
 
 
-def config0(seed: int = 1000):
+def tiny_ragged(seed: int = 1000):
     """Tiny ragged forward: B=2, lengths [3,5], nk=1, nv=2, K=V=16, float32
     pool of 4 slots (std 0.1), slot_idx [3,1], scale 1/4, L2 norm on."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -86,7 +86,7 @@ def config0(seed: int = 1000):
     return w
 
 
-def config1(seed: int = 1001, batch: int = 256, slots: int = 512):
+def decode_step(seed: int = 1001, batch: int = 256, slots: int = 512):
     """Decode step: 256 sequences of one token, nk=16, nv=32, K=V=128, bf16
     pool of 512 slots (std 0.05), distinct random slots."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -94,7 +94,7 @@ def config1(seed: int = 1001, batch: int = 256, slots: int = 512):
                          state_dtype="bf16", state_sigma=0.05)
 
 
-def config2(seed: int = 1002, batch: int = 8, max_len: int = 4096, slots: int = 64):
+def ragged_prefill(seed: int = 1002, batch: int = 8, max_len: int = 4096, slots: int = 64):
     """Ragged prefill: 8 rows, lengths uniform in [1, 4096], heads as the
     decode step, bf16 pool of 64 slots (std 0.05), state in place."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -103,8 +103,8 @@ def config2(seed: int = 1002, batch: int = 8, max_len: int = 4096, slots: int = 
                          state_dtype="bf16", state_sigma=0.05)
 
 
-def config3(seed: int = 1003, batch: int = 64, max_window: int = 12, ring_len: int = 8,
-            slots: int = 128):
+def verify_window(seed: int = 1003, batch: int = 64, max_window: int = 12, ring_len: int = 8,
+                  slots: int = 128):
     """Speculative verify plus fold: 64 rows with windows uniform in [1, 12],
     ring_len 8, float32 ring and bf16 pool of 128 slots each; the accepted
     count is uniform in [0, len] for rows that fit the ring and the full
@@ -155,7 +155,7 @@ def gdp_inputs(rng, B, S_draft, M, H, HV, K, V, slots, pad_frac, state_sigma,
                 scale=K ** -0.5)
 
 
-def config4(seed: int = 1004, batch: int = 128, slots: int = 256):
+def gdp_decode(seed: int = 1004, batch: int = 128, slots: int = 256):
     """GDP decode: M=2 copies x S=4 drafts (T=8, steps_per_token=2), B=128 with
     10% padding, H=16, HV=32, K=V=128, bf16 state of 256 slots, intermediate
     buffer [256, 4, 32, 128, 128]."""
@@ -164,4 +164,6 @@ def config4(seed: int = 1004, batch: int = 128, slots: int = 256):
                       pad_frac=0.1, state_sigma=0.05)
 
 
-CONFIGS = {0: config0, 1: config1, 2: config2, 3: config3, 4: config4}
+WORKLOADS = {"tiny_ragged": tiny_ragged, "decode_step": decode_step,
+             "ragged_prefill": ragged_prefill, "verify_window": verify_window,
+             "gdp_decode": gdp_decode}

@@ -56,16 +56,16 @@ def check_fwd_against_oracle(w, name, gpu=None, **kw):
 
 # ------------------------------------------------------------ the configs ---
 
-def test_c0_tiny_ragged_fwd():
-    say("config 0: B=2 L=[3,5] nk=1 nv=2 K=V=16 f32 pool")
-    w = wl.config0()
-    check_fwd_against_oracle(w, "c0")
+def test_tiny_ragged_fwd():
+    say("tiny ragged forward: B=2 L=[3,5] nk=1 nv=2 K=V=16 f32 pool")
+    w = wl.tiny_ragged()
+    check_fwd_against_oracle(w, "tiny")
 
 
-def test_c1_decode():
-    say("config 1: decode B=256 nk=16 nv=32 K=V=128 bf16 pool 512")
-    w = wl.config1()
-    check_fwd_against_oracle(w, "c1")
+def test_decode_step():
+    say("decode step: B=256 x 1 token nk=16 nv=32 K=V=128 bf16 pool 512")
+    w = wl.decode_step()
+    check_fwd_against_oracle(w, "decode")
 
 
 def sub_packed(w, rows, key_heads):
@@ -92,10 +92,10 @@ def sub_packed(w, rows, key_heads):
     return sub, toks, vheads
 
 
-def test_c2_prefill_sampled():
-    w = wl.config2()
+def test_ragged_prefill_sampled():
+    w = wl.ragged_prefill()
     lens = np.diff(w["row_offsets"].astype(np.int64))
-    say(f"config 2: prefill B=8 lengths {lens.tolist()} (GPU full, oracle sampled)")
+    say(f"ragged prefill: B=8 lengths {lens.tolist()} (GPU full, oracle sampled)")
     out_g, st_g = H.gpu_fwd(w)
     assert np.isfinite(out_g).all()
     longest = int(np.argmax(lens))
@@ -106,11 +106,11 @@ def test_c2_prefill_sampled():
         _, unr = oracle_fwd(sub, state=H.f32_pool(sub["state"]))
         V = w["state"].shape[3]
         cols = np.concatenate([np.arange(hv * V, (hv + 1) * V) for hv in vheads])
-        err = H.assert_close(out_g[np.ix_(toks, cols)], out_r, f"c2 rows {rows} out")
+        err = H.assert_close(out_g[np.ix_(toks, cols)], out_r, f"prefill rows {rows} out")
         sl = sub["slot_idx"].astype(np.int64)
-        ties = H.assert_state_close(st_g[sl][:, vheads], st_r[sl], f"c2 rows {rows} state",
+        ties = H.assert_state_close(st_g[sl][:, vheads], st_r[sl], f"prefill rows {rows} state",
                                     unr[sl])
-        say(f"c2 rows {rows} key heads {kh}: out rel err {err:.2e}, ties {ties}")
+        say(f"prefill rows {rows} key heads {kh}: out rel err {err:.2e}, ties {ties}")
     others = np.setdiff1d(np.arange(64), w["slot_idx"].astype(np.int64))
     assert np.array_equal(st_g[others], w["state"][others])
 
@@ -122,15 +122,15 @@ def verify_oracle(w, state=None):
     return oracle.recurrence_verify_ring(**args)
 
 
-def test_c3_verify_and_fold():
-    w = wl.config3()
+def test_verify_window_and_fold():
+    w = wl.verify_window()
     lens = np.diff(w["row_offsets"].astype(np.int64))
     ring_len = w["ring"].shape[2]
-    say(f"config 3: verify+fold B=64 windows in [1,12] ring_len {ring_len}, "
+    say(f"verify window + fold: B=64 windows in [1,12] ring_len {ring_len}, "
         f"{int((lens > ring_len).sum())} long rows")
     out_g, st_g, ring_g = H.gpu_verify(w)
     out_r, st_r, ring_r = verify_oracle(w)
-    H.assert_close(out_g, out_r, "c3 verify output")
+    H.assert_close(out_g, out_r, "verify verify output")
     # GPU identity: verify output == forward output, bit for bit
     out_f, st_f = H.gpu_fwd(w)
     assert np.array_equal(out_g.view(np.uint32), out_f.view(np.uint32)), "verify != fwd output"
@@ -141,7 +141,7 @@ def test_c3_verify_and_fold():
             assert np.array_equal(st_g[s], w["state"][s]), f"row {b}: verify wrote the state"
         else:               # committed like the forward, bit for bit, and no records
             assert np.array_equal(st_g[s], st_f[s]), f"row {b}: long row commit != fwd"
-            H.assert_state_close(st_g[s], st_r[s], f"c3 row {b} commit", unr_v[s])
+            H.assert_state_close(st_g[s], st_r[s], f"verify row {b} commit", unr_v[s])
             assert not ring_g[w["ring_slot_idx"][b]].any(), f"row {b}: long row recorded"
     # ring records against the oracle's (only entries the rows wrote)
     G = 2
@@ -152,7 +152,7 @@ def test_c3_verify_and_fold():
         rr = w["ring_slot_idx"][b]
         got = ring_g[rr, :, :L, :K + G * (V + 1)]
         ref = ring_r[rr, :, :L, :K + G * (V + 1)]
-        H.assert_close(got, ref, f"c3 ring row {b}")
+        H.assert_close(got, ref, f"verify ring row {b}")
     # fold with the configured accepted counts
     acc = w["accepted"]
     st_fold_g = H.gpu_fold(w, st_g, ring_g, acc)
@@ -163,7 +163,7 @@ def test_c3_verify_and_fold():
                               ring_slot_idx=w["ring_slot_idx"], accepted=acc,
                               num_value_heads=32, num_key_heads=16)
     sl = touched(w)
-    ties = H.assert_state_close(st_fold_g[sl], st_fold_r[sl], "c3 fold state", unr_f[sl])
+    ties = H.assert_state_close(st_fold_g[sl], st_fold_r[sl], "verify fold state", unr_f[sl])
     # GPU identity: fold(n) == forward over the first n tokens, bit for bit
     pre_len = [int(a) for a in acc]
     off = w["row_offsets"].astype(np.int64)
@@ -176,7 +176,7 @@ def test_c3_verify_and_fold():
     for b, L in enumerate(lens):
         s = w["slot_idx"][b]
         assert np.array_equal(st_fold_g[s], st_pre[s]), f"row {b}: fold({acc[b]}) != fwd prefix"
-    say(f"c3: verify/fold parity ok, fold ties {ties}")
+    say(f"verify: verify/fold parity ok, fold ties {ties}")
 
 
 def fused_oracle(w, f32=False):
@@ -190,19 +190,19 @@ def fused_oracle(w, f32=False):
     return oracle.fused_recurrent_update(**args)
 
 
-def test_c4_gdp_decode():
-    w = wl.config4()
+def test_gdp_decode():
+    w = wl.gdp_decode()
     idx = w["state_indices"]
-    say(f"config 4: GDP decode B=128 T=8 spt=2, {int((idx < 0).sum())} padding rows")
+    say(f"GDP decode: B=128 T=8 spt=2, {int((idx < 0).sum())} padding rows")
     o_g, st_g, inter_g = H.gpu_fused(w)
     o_r, st_r, inter_r = fused_oracle(w)
     o_u, st_u, inter_u = fused_oracle(w, f32=True)
-    err = H.assert_close(o_g, o_r, "c4 output")
+    err = H.assert_close(o_g, o_r, "gdp output")
     pad = idx < 0
     assert np.array_equal(o_g[pad].view(np.uint32), np.zeros_like(o_g[pad]).view(np.uint32))
     sl = idx[~pad].astype(np.int64)
-    ties = H.assert_state_close(st_g[sl], st_r[sl], "c4 state", st_u[sl])
-    ties += H.assert_state_close(inter_g[sl], inter_r[sl], "c4 snapshots", inter_u[sl])
+    ties = H.assert_state_close(st_g[sl], st_r[sl], "gdp state", st_u[sl])
+    ties += H.assert_state_close(inter_g[sl], inter_r[sl], "gdp snapshots", inter_u[sl])
     others = np.setdiff1d(np.arange(256), sl)
     assert np.array_equal(st_g[others], w["state"][others])
     assert np.array_equal(inter_g[others], w["intermediate_states"][others])
@@ -211,10 +211,10 @@ def test_c4_gdp_decode():
     # GDP caller slicing: the answer of draft token i is on copy M-1
     M = w["steps_per_token"]
     assert o_g[:, M - 1::M].shape[1] == 4
-    say(f"c4: out rel err {err:.2e}, state+snapshot ties {ties}")
+    say(f"gdp: out rel err {err:.2e}, state+snapshot ties {ties}")
 
 
-def test_c4_snapshot_equals_prefix_run():
+def test_snapshot_equals_prefix_run():
     """intermediate[slot, i] equals the state of a GPU run over the first
     (i+1)*spt steps, bit for bit."""
     rng = np.random.Generator(np.random.PCG64(77))
