@@ -125,19 +125,24 @@ gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t G, int64_t total_tokens,
         } else if (long_rows) {
             s.cpl = GDR_LONG_CPL;
             s.chunk = GDR_LONG_CHUNK;
+            s.kg_low = GDR_LONG_KGLOW;
         } else if (e == Entry::Fused && !decode) {
             s.cpl = GDR_FUSED_CPL;
             s.chunk = GDR_FUSED_CHUNK;
+            s.kg_low = GDR_FUSED_KGLOW;
         } else if (decode) {
             s.cpl = GDR_DECODE_CPL;
             s.chunk = GDR_DECODE_CHUNK;
+            s.kg_low = GDR_DECODE_KGLOW;
         } else {
             s.cpl = GDR_SHORT_CPL;
             s.chunk = GDR_SHORT_CHUNK;
+            s.kg_low = GDR_SHORT_KGLOW;
         }
     } else if (long_rows && e != Entry::Fold) {
         s.cpl = 2;
         s.chunk = 16;
+        s.kg_low = true;
     } else {
         s.cpl = K == 64 ? 8 : (K == 32 ? 4 : 2);
         s.chunk = 8;

@@ -60,6 +60,7 @@ struct LaunchShape {
     int cpl;        // value columns per lane (8 lanes share one key-row group)
     int chunk;      // tokens staged per barrier
     int wpg;        // waves per workgroup
+    bool kg_low;    // lane layout: row group in the low lane bits
 };
 
 // Host-side launchers (defined next to the kernels).  Return hipError_t.
@@ -95,6 +96,18 @@ hipError_t launch_fold(const FoldParams& p, const LaunchShape& s, StateType st,
 #endif
 #ifndef GDR_LONG_CHUNK
 #define GDR_LONG_CHUNK 16
+#endif
+#ifndef GDR_DECODE_KGLOW
+#define GDR_DECODE_KGLOW false
+#endif
+#ifndef GDR_SHORT_KGLOW
+#define GDR_SHORT_KGLOW false
+#endif
+#ifndef GDR_FUSED_KGLOW
+#define GDR_FUSED_KGLOW false
+#endif
+#ifndef GDR_LONG_KGLOW
+#define GDR_LONG_KGLOW true
 #endif
 #ifndef GDR_FOLD_CPL
 #define GDR_FOLD_CPL 4

@@ -7,14 +7,15 @@
 //
 // Work decomposition (ours, for 64-wide waves):
 //   * one wave owns the full K extent of BV = 8*CPL contiguous value columns of
-//     one value head: lane = 8*kg + vl holds key rows [kg*R, kg*R + R) (R = K/8)
-//     of columns [j0, j0 + CPL).  The state stays in VGPRs for the whole row.
+//     one value head: lane = 8*vl + kg holds key rows [kg*R, kg*R + R) (R = K/8)
+//     of columns [j0, j0 + CPL), j0 = 8*CPL*tile + CPL*vl.  The state stays in
+//     VGPRs for the whole row.
 //   * the K-reduction of every column (S^T k_hat and S^T q_hat) is an in-lane
 //     fused multiply-add chain over the R rows in ascending order followed by
-//     an xor butterfly over the 8 lane groups (DPP row_ror:8, then gfx950's
-//     v_permlane16_swap / v_permlane32_swap).  This order depends on K only,
-//     never on CPL, the chunk size or the workgroup shape, so every launch
-//     shape, the verify kernel and the fold produce identical bits.
+//     a butterfly over the 8 row groups, which are the 8 lanes of one DPP
+//     half-row (three DPP adds).  This order depends on K only, never on CPL,
+//     the chunk size or the workgroup shape, so every launch shape, the verify
+//     kernel and the fold produce identical bits.
 //   * a workgroup is WPG waves of one (row, key head); q/k of a chunk of C
 //     tokens are normalised once per workgroup and staged in LDS together with
 //     the chunk's v, decay and beta; the next chunk's global loads are issued
@@ -52,11 +53,21 @@ __device__ __forceinline__ float xor32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 8 key-row groups (lanes l, l^8, ..., l^56).
+// Sum over the 8 key-row groups of a column, identical in all 8 lanes that
+// hold them.  Both lane layouts (row group in the low or in the high three
+// lane bits) add the groups as ((g0+g1)+(g2+g3)) + ((g4+g5)+(g6+g7)), so they
+// give identical bits.
+template <bool KG_LOW>
 __device__ __forceinline__ float sum_row_groups(float x) {
-    x = x + dpp<0x128>(x);  // row_ror:8 is lane ^ 8 inside a 16-lane row
-    x = xor16_sum(x);
-    x = xor32_sum(x);
+    if constexpr (KG_LOW) {  // the 8 groups are the 8 lanes of one half-row
+        x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+        x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+        x = x + dpp<0x141>(x);  // row_half_mirror: quads are uniform, pairs quad 0/1
+    } else {                 // the groups are lanes l, l^8, ..., l^56
+        x = x + dpp<0x128>(x);  // row_ror:8 is lane ^ 8 inside a 16-lane row
+        x = xor16_sum(x);
+        x = xor32_sum(x);
+    }
     return x;
 }
 
@@ -202,6 +213,8 @@ __device__ __forceinline__ int pad_index(int i) { return i + (i / R) * 4; }
 
 // ------------------------------------------------------------- recurrence ---
 
+enum : int { kPlain = 0, kVerify = 1, kSnap = 2 };
+
 // One work item: value columns [j0, j0 + CPL) of every key row, for one value
 // head of one row, resolved once per item.
 struct Item {
@@ -211,7 +224,7 @@ struct Item {
     bool pad, record;
 };
 
-template <int K, int CPL, int C, int WPG, typename ST>
+template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW>
 struct Rec {
     static constexpr int V = K;
     static constexpr int R = K / kRowGroups;
@@ -238,6 +251,12 @@ struct Rec {
         float q[SPW][QK], k[SPW][QK], v[VPL], a, b;
     };
 
+    // Lane = 8 * column chunk + row group (KG_LOW) or 8 * row group + column
+    // chunk.  The first keeps each reduction inside a DPP half-row; the second
+    // keeps 8 consecutive lanes on one contiguous run of a state row.
+    __device__ static int row_group(int lane) { return KG_LOW ? (lane & 7) : (lane >> 3); }
+    __device__ static int col_chunk(int lane) { return KG_LOW ? (lane >> 3) : (lane & 7); }
+
     __device__ static Item item(const RecParams& p, int idx, int w, int lane) {
         Item it;
         int blk = idx;
@@ -249,7 +268,7 @@ struct Rec {
         it.m = unit / TILES;
         it.vt = unit - it.m * TILES;
         it.hv = it.h * p.G + it.m;
-        it.j0 = it.vt * BV + (lane & 7) * CPL;
+        it.j0 = it.vt * BV + col_chunk(lane) * CPL;
         if (p.offsets) {
             const int64_t t0 = p.offsets[it.row];
             it.L = static_cast<int>(static_cast<int64_t>(p.offsets[it.row + 1]) - t0);
@@ -279,7 +298,7 @@ struct Rec {
 
     // Padding request: +0.0 output for every token, nothing else.
     __device__ static void zero_output(const RecParams& p, const Item& it, int lane) {
-        if ((lane >> 3) != 0) return;
+        if (row_group(lane) != 0) return;
         float z[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) z[c] = 0.0f;
@@ -420,31 +439,44 @@ struct Rec {
 
     // The tokens of chunk c, staged in B.  The state before the chunk is
     // scale * S; both are updated (see decay_step for the representation).
+    // REC: record the ring for rows that fit it (verify); SNAP: store snapshots.
+    template <bool REC, bool SNAP>
     __device__ static void run_chunk(const RecParams& p, const Item& it, int c, const float* B,
                                      float (&S)[R][CPL], float& scale, int w, int lane) {
-        const int kg = lane >> 3;
+        const int kg = row_group(lane);
+        const int vc = col_chunk(lane) * CPL;
         const int tc = c * C;
         const int Lc = min(C, it.L - tc);
-        float* outp = out_ptr(p, it);
-        float* rec = it.record ? p.ring + static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
-                                     static_cast<int64_t>(it.h) * p.ring_head
-                               : nullptr;
+        float* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
+        float* rec = nullptr;
+        if (REC && it.record)
+            rec = p.ring + static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
+                  static_cast<int64_t>(it.h) * p.ring_head + static_cast<int64_t>(tc) * p.ring_tok;
+        ST* snap = nullptr;
+        int snap_left = 0;
+        if constexpr (SNAP) {  // steps until the next snapshot, and its entry
+            const int done = tc % p.spt;
+            snap_left = p.spt - done;
+            snap = static_cast<ST*>(p.snap) + static_cast<int64_t>(it.slot) * p.snap_slot +
+                   static_cast<int64_t>(tc / p.spt) * p.snap_tok +
+                   static_cast<int64_t>(it.hv) * p.snap_head + it.j0;
+        }
+        int snap_i = SNAP ? tc / p.spt : 0;
 
         float kr[R];
         read_rows<R>(B + OFF_K, kg, kr);
-        float x[CPL];  // S^T k_hat of the next token, before the scale
+        float x[CPL];  // S^T k_hat of the current token, before the scale
         dot_rows<R, CPL>(S, kr, x);
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups(x[cc]);
+        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
 
         for (int tau = 0; tau < Lc; ++tau) {
             const float a = B[OFF_A + w * C + tau];
             const float be = B[OFF_B + w * C + tau];
             float vv[CPL];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc)
-                vv[cc] = B[OFF_V + w * VTOT + tau * BV + (lane & 7) * CPL + cc];
-            // r = S_{t-1}^T k_hat with the decay of this token: (scale * a) * x
+            for (int cc = 0; cc < CPL; ++cc) vv[cc] = B[OFF_V + w * VTOT + tau * BV + vc + cc];
+            // r = S_{t-1}^T k_hat with this token's decay: (scale * a) * x
             const float cn = scale * a;
             float u[CPL];
 #pragma unroll
@@ -462,36 +494,45 @@ struct Rec {
             read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
             float o[CPL];
             dot_rows<R, CPL>(S, qr, o);
-            const bool more = tau + 1 < Lc;
-            if (more) {
+            if (C > 1 && tau + 1 < Lc) {
                 read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
                 dot_rows<R, CPL>(S, kr, x);
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups(x[cc]);
+                for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
             }
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups(o[cc]);
+            for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups<KG_LOW>(o[cc]);
 
-            const int t = tc + tau;
-            if (kg == 0) store_cols<CPL>(outp + t * p.o_tok, o);
-            if (it.record) {
-                float* r = rec + t * p.ring_tok;
-                if (kg == 0) store_cols<CPL>(r + K + it.m * V + it.j0, u);
-                if (it.vt == 0 && lane == 0) r[K + p.G * V + it.m] = a;
+            if (kg == 0) store_cols<CPL>(outp, o);
+            outp += p.o_tok;
+            if (REC && it.record) {
+                if (kg == 0) store_cols<CPL>(rec + K + it.m * V + it.j0, u);
+                if (it.vt == 0 && lane == 0) rec[K + p.G * V + it.m] = a;
+                rec += p.ring_tok;
             }
-            if (p.snap && (t + 1) % p.spt == 0) {
-                const int i = (t + 1) / p.spt - 1;
-                if (i < p.snap_count)
-                    store_tile(static_cast<ST*>(p.snap) + static_cast<int64_t>(it.slot) * p.snap_slot +
-                                   static_cast<int64_t>(i) * p.snap_tok +
-                                   static_cast<int64_t>(it.hv) * p.snap_head + it.j0,
-                               kg, scale, S);
+            if constexpr (SNAP) {
+                if (--snap_left == 0) {
+                    snap_left = p.spt;
+                    if (snap_i < p.snap_count) store_tile(snap, kg, scale, S);
+                    ++snap_i;
+                    snap += p.snap_tok;
+                }
             }
         }
     }
 
+    // MODE: kPlain (forward, fused update without snapshots), kVerify (rows
+    // that fit the ring record it; longer rows run as kPlain), kSnap.
+    template <int MODE>
+    __device__ static void run_chunk_mode(const RecParams& p, const Item& it, int c,
+                                          const float* B, float (&S)[R][CPL], float& scale, int w,
+                                          int lane) {
+        run_chunk<MODE == kVerify, MODE == kSnap>(p, it, c, B, S, scale, w, lane);
+    }
+
     // All chunks of an item whose state is scale * S and whose chunk-0 inputs
     // are in st.
+    template <int MODE>
     __device__ static void run_item(const RecParams& p, const Item& it, float (&S)[R][CPL],
                                     float& scale, Stage& st, float* lds, int w, int lane) {
         commit_stage(p, it, 0, st, lds, w, lane);
@@ -500,7 +541,7 @@ struct Rec {
         for (int c = 0; c < nch; ++c) {
             const bool next = c + 1 < nch;
             if (next) load_stage(p, it, c + 1, st, w, lane);
-            run_chunk(p, it, c, lds + (c & 1) * BUF, S, scale, w, lane);
+            run_chunk_mode<MODE>(p, it, c, lds + (c & 1) * BUF, S, scale, w, lane);
             if (next) {
                 commit_stage(p, it, c + 1, st, lds + ((c + 1) & 1) * BUF, w, lane);
                 __syncthreads();
@@ -510,13 +551,17 @@ struct Rec {
 };
 
 // One work item per workgroup.
-template <int K, int CPL, int C, int WPG, typename ST>
-__global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
-    using Q = Rec<K, CPL, C, WPG, ST>;
+// One-token stages are the HBM-bound decode shape: ask for 4 waves per SIMD.
+template <int C>
+constexpr int kMinWaves = C == 1 ? 4 : 1;
+
+template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, int MODE>
+__global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecParams p) {
+    using Q = Rec<K, CPL, C, WPG, ST, KG_LOW>;
     __shared__ __attribute__((aligned(16))) float lds[2 * Q::BUF];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int kg = lane >> 3;
+    const int kg = Q::row_group(lane);
     const Item it = Q::item(p, blockIdx.x, w, lane);
     if (it.pad) {
         Q::zero_output(p, it, lane);
@@ -528,7 +573,7 @@ __global__ void __launch_bounds__(WPG * 64) rec_kernel(const RecParams p) {
     float scale = 1.0f;
     typename Q::Stage st;
     Q::load_stage(p, it, 0, st, w, lane);
-    Q::run_item(p, it, S, scale, st, lds, w, lane);
+    Q::template run_item<MODE>(p, it, S, scale, st, lds, w, lane);
     Q::store_state(p, it, kg, scale, S);
 }
 
@@ -543,7 +588,7 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int kg = lane >> 3;
+    const int kg = lane >> 3;  // 8 consecutive lanes cover one contiguous row run
     const int vl = lane & 7;
     int blk = blockIdx.x;
     const int part = blk % p.parts;
@@ -607,34 +652,47 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
 
 // ------------------------------------------------------------- dispatch ---
 
-template <int K, int CPL, int C, typename ST>
-static hipError_t launch_rec_wpg(const RecParams& p, int wpg, hipStream_t stream) {
+template <int K, int CPL, int C, typename ST, bool KG_LOW, int MODE>
+static hipError_t launch_rec_mode(const RecParams& p, int wpg, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.rows) * p.nk * p.parts);
-    switch (wpg) {
-        case 1: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 1, ST>), grid, dim3(64), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 2, ST>), grid, dim3(128), 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST>), grid, dim3(256), 0, stream, p); break;
-        default: return hipErrorInvalidValue;
+    constexpr int TILES = K / (kLanesPerRow * CPL);
+    if constexpr (TILES % 4 == 0) {  // every head splits into a multiple of 4 waves
+        if (wpg != 4) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, MODE>), grid, dim3(256), 0, stream, p);
+    } else {
+        switch (wpg) {
+            case 1: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 1, ST, KG_LOW, MODE>), grid, dim3(64), 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 2, ST, KG_LOW, MODE>), grid, dim3(128), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, MODE>), grid, dim3(256), 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
 
+template <int K, int CPL, int C, typename ST, bool KG_LOW>
+static hipError_t launch_rec_wpg(const RecParams& p, int wpg, hipStream_t stream) {
+    if (p.ring) return launch_rec_mode<K, CPL, C, ST, KG_LOW, kVerify>(p, wpg, stream);
+    if (p.snap) return launch_rec_mode<K, CPL, C, ST, KG_LOW, kSnap>(p, wpg, stream);
+    return launch_rec_mode<K, CPL, C, ST, KG_LOW, kPlain>(p, wpg, stream);
+}
+
 template <typename ST>
 static hipError_t launch_rec_st(const RecParams& p, const LaunchShape& s, hipStream_t stream) {
-#define GDR_REC_CASE(KK, CC, CH)                                   \
-    if (s.K == KK && s.cpl == CC && s.chunk == CH)                 \
-        return launch_rec_wpg<KK, CC, CH, ST>(p, s.wpg, stream);
-    GDR_REC_CASE(128, GDR_DECODE_CPL, GDR_DECODE_CHUNK)
-    GDR_REC_CASE(128, GDR_SHORT_CPL, GDR_SHORT_CHUNK)
-    GDR_REC_CASE(128, GDR_FUSED_CPL, GDR_FUSED_CHUNK)
-    GDR_REC_CASE(128, GDR_LONG_CPL, GDR_LONG_CHUNK)
+#define GDR_REC_CASE(KK, CC, CH, KL)                                              \
+    if (s.K == KK && s.cpl == CC && s.chunk == CH && s.kg_low == KL)             \
+        return launch_rec_wpg<KK, CC, CH, ST, KL>(p, s.wpg, stream);
+    GDR_REC_CASE(128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
+    GDR_REC_CASE(128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
+    GDR_REC_CASE(128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
+    GDR_REC_CASE(128, GDR_LONG_CPL, GDR_LONG_CHUNK, GDR_LONG_KGLOW)
 #ifndef GDR_ONLY_K128
-    GDR_REC_CASE(64, 8, 8)
-    GDR_REC_CASE(64, 2, 16)
-    GDR_REC_CASE(32, 4, 8)
-    GDR_REC_CASE(32, 2, 16)
-    GDR_REC_CASE(16, 2, 8)
-    GDR_REC_CASE(16, 2, 16)
+    GDR_REC_CASE(64, 8, 8, false)
+    GDR_REC_CASE(64, 2, 16, true)
+    GDR_REC_CASE(32, 4, 8, false)
+    GDR_REC_CASE(32, 2, 16, true)
+    GDR_REC_CASE(16, 2, 8, false)
+    GDR_REC_CASE(16, 2, 16, true)
 #endif
 #undef GDR_REC_CASE
     return hipErrorInvalidValue;
