@@ -188,6 +188,7 @@ def case_verify_fold(torch, gdr, B, wl, rotations):
 
 def case_gdp(torch, gdr, B, wl, rotations):
     launches = []
+    rb_sets = []
     w0 = None
     for r in range(rotations):
         w = wl.gdp_decode(seed=1004 + 100 * r)
@@ -208,16 +209,36 @@ def case_gdp(torch, gdr, B, wl, rotations):
             rc = L.gdr_fused_recurrent_update(*args)
             assert rc == 0, B.gdr_last_error_message()
         launches.append(launch)
+        rb_sets.append((t, ds, L))
     idx = w0["state_indices"]
     act = int((idx >= 0).sum())
+    # rollback after verification: request n accepts (n mod 5) draft tokens
+    acc = np.resize(np.arange(5, dtype=np.int32), len(idx))
+    rb_launches = []
+    for t, ds, L_ in rb_sets:
+        a_t = _dev(torch, acc)
+        a_d = B.describe(a_t)
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        rargs = (ctypes.byref(ds["state"]), ctypes.byref(ds["idx"]),
+                 ctypes.byref(ds["intermediate_states"]), ctypes.byref(a_d), st)
+
+        def rollback(rargs=rargs, keep=(t, ds, a_t, a_d)):
+            rc = L_.gdr_snapshot_rollback(*rargs)
+            assert rc == 0, B.gdr_last_error_message()
+        rb_launches.append(rollback)
+    rolled = int(((idx >= 0) & (acc >= 1) & (acc <= 4)).sum())
     HV, H, K, V, T = 32, 16, 128, 128, 8
     head = K * V * 2
     state = act * HV * head * 2 + act * HV * head * (T // 2)
     inputs = act * T * (2 * H * K + HV * V + 2 * HV) * 4
     outs = 128 * T * HV * V * 4
-    return Case("gdp_128x8", launches, state + inputs + outs, state, act * T,
-                FLOPS_PER_TOKEN_HEAD_ELEM * act * T * HV * K * V,
-                extra={"active_rows": act, "draft_tokens": act * T // 2})
+    gdp = Case("gdp_128x8", launches, state + inputs + outs, state, act * T,
+               FLOPS_PER_TOKEN_HEAD_ELEM * act * T * HV * K * V,
+               extra={"active_rows": act, "draft_tokens": act * T // 2})
+    rb_bytes = rolled * HV * head * 2
+    rb = Case("rollback_128x4", rb_launches, rb_bytes, rb_bytes, rolled,
+              extra={"rolled_rows": rolled})
+    return gdp, rb
 
 
 # ----------------------------------------------------------------- timing ---
@@ -321,7 +342,7 @@ def main():
     if "verify" in only:
         cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations))
     if "gdp" in only:
-        cases.append(case_gdp(torch, gdr, B, wl, 2))
+        cases.extend(case_gdp(torch, gdr, B, wl, 2))
     torch.cuda.synchronize()
 
     results = {}

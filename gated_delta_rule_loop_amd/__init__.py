@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     gdr_recurrence_fwd,
     gdr_recurrence_verify_ring,
     gdr_ring_record_elements,
+    gdr_snapshot_rollback,
     gdr_state_fold,
     gdr_version,
     lib,

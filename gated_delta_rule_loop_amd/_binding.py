@@ -41,8 +41,8 @@ class GdrError(RuntimeError):
 
 _lib = None
 EXPORTS = ("gdr_recurrence_fwd", "gdr_recurrence_verify_ring", "gdr_state_fold",
-           "gdr_fused_recurrent_update", "gdr_fwd_output_shape", "gdr_ring_record_elements",
-           "gdr_last_error_message", "gdr_version")
+           "gdr_fused_recurrent_update", "gdr_snapshot_rollback", "gdr_fwd_output_shape",
+           "gdr_ring_record_elements", "gdr_last_error_message", "gdr_version")
 
 
 def lib():
@@ -60,12 +60,13 @@ def lib():
         L.gdr_state_fold.argtypes = [i32, i32, P, P, P, P, P, vp]
         L.gdr_fused_recurrent_update.argtypes = [P, P, P, P, P, f32, P, P, u32, P, P, P, P, i32,
                                                  P, vp]
+        L.gdr_snapshot_rollback.argtypes = [P, P, P, P, vp]
         L.gdr_fwd_output_shape.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64)]
         L.gdr_ring_record_elements.argtypes = [i32, i32, i32]
         L.gdr_ring_record_elements.restype = ctypes.c_int64
         L.gdr_last_error_message.restype = ctypes.c_char_p
         L.gdr_version.restype = ctypes.c_char_p
-        for name in EXPORTS[:5]:
+        for name in EXPORTS[:6]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -179,6 +180,16 @@ def gdr_fused_recurrent_update(q, k, v, g=None, beta=None, scale=None, initial_s
                                           _stream(stream))
     _check("gdr_fused_recurrent_update", rc)
     return o, (state if state is not None else final_state)
+
+
+def gdr_snapshot_rollback(state, state_indices, intermediate_states, accepted, *,
+                          stream=None):
+    """Roll each request's state back to its snapshot after `accepted` draft
+    tokens (page "core.ssm.ops.gdp.fused_recurrent", intermediate_states)."""
+    ds = [describe(x) for x in (state, state_indices, intermediate_states, accepted)]
+    rc = lib().gdr_snapshot_rollback(*[_ref(d) for d in ds], _stream(stream))
+    _check("gdr_snapshot_rollback", rc)
+    return state
 
 
 def gdr_fwd_output_shape(qkv_conv_output, recurrent_state):

@@ -501,6 +501,49 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     return hip_status(fn, gdr::launch_recurrence(p, s, st, static_cast<hipStream_t>(stream)));
 }
 
+int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indices,
+                          const gdr_tensor* intermediate_states, const gdr_tensor* accepted,
+                          void* stream) {
+    const char* fn = "gdr_snapshot_rollback";
+    int rc;
+    if ((rc = check_state(fn, "state", state, 4, nullptr))) return rc;
+    const int64_t S = state->shape[0], HV = state->shape[1], K = state->shape[2],
+                  V = state->shape[3];
+    const int64_t ishape[5] = {S, -1, HV, K, V};
+    if ((rc = check_state(fn, "intermediate_states", intermediate_states, 5, ishape))) return rc;
+    if (intermediate_states->dtype != state->dtype)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: intermediate_states must match the state dtype", fn);
+    if (!present(state_indices)) return fail(GDR_ERR_INVALID_ARG, "%s: state_indices is null", fn);
+    const int64_t N = state_indices->shape[0];
+    if ((rc = check_index_vec(fn, "state_indices", state_indices, N))) return rc;
+    if ((rc = check_index_vec(fn, "accepted", accepted, N))) return rc;
+    if (N == 0 || HV == 0 || intermediate_states->shape[1] == 0) {
+        g_last_error.clear();
+        return GDR_OK;
+    }
+    const int64_t es = state->dtype == GDR_DTYPE_BF16 ? 2 : 4;
+    const int64_t block16 = K * V * es / 16;
+    const int64_t per_wg = int64_t{gdr::kRollbackThreads} * gdr::kRollbackPerThread;
+    gdr::RollbackParams p{};
+    p.rows = static_cast<int32_t>(N);
+    p.HV = static_cast<int32_t>(HV);
+    p.chunks = static_cast<int32_t>((block16 + per_wg - 1) / per_wg);
+    if (N * HV * p.chunks > (int64_t{1} << 31) - 1)
+        return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
+    p.idx = static_cast<const int32_t*>(state_indices->data);
+    p.accepted = static_cast<const int32_t*>(accepted->data);
+    p.state = state->data;
+    p.st_slot = state->stride[0] * es;
+    p.st_head = state->stride[1] * es;
+    p.inter = intermediate_states->data;
+    p.in_slot = intermediate_states->stride[0] * es;
+    p.in_tok = intermediate_states->stride[1] * es;
+    p.in_head = intermediate_states->stride[2] * es;
+    p.int_tokens = static_cast<int32_t>(intermediate_states->shape[1]);
+    p.block16 = block16;
+    return hip_status(fn, gdr::launch_rollback(p, static_cast<hipStream_t>(stream)));
+}
+
 int gdr_fwd_output_shape(const gdr_tensor* qkv_conv_output, const gdr_tensor* recurrent_state,
                          int64_t out_shape[2]) {
     const char* fn = "gdr_fwd_output_shape";

@@ -52,6 +52,16 @@ struct FoldParams {
     const uint32_t* accepted;
 };
 
+struct RollbackParams {
+    int32_t rows, HV, chunks;  // workgroups per (request, head) = chunks
+    const int32_t* idx;        // state_indices (-1 = padding)
+    const int32_t* accepted;
+    void* state; int64_t st_slot, st_head;                       // bytes
+    const void* inter; int64_t in_slot, in_tok, in_head;         // bytes
+    int32_t int_tokens;
+    int64_t block16;           // 16-byte units per (slot, head) block
+};
+
 enum class StateType { F32 = 0, BF16 = 1 };
 
 // Launch configuration picked by the host for one call.
@@ -68,6 +78,9 @@ hipError_t launch_recurrence(const RecParams& p, const LaunchShape& s, StateType
                              hipStream_t stream);
 hipError_t launch_fold(const FoldParams& p, const LaunchShape& s, StateType st,
                        hipStream_t stream);
+hipError_t launch_rollback(const RollbackParams& p, hipStream_t stream);
+constexpr int kRollbackThreads = 256;
+constexpr int kRollbackPerThread = 8;  // 16-byte vectors per thread
 
 // Launch profiles at K = 128 (value columns per lane, tokens per stage).  The
 // reduction order does not depend on them, so they are free tuning choices:

@@ -648,7 +648,45 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
     }
 }
 
+// -------------------------------------------------------------- rollback ---
+
+// state[slot, hv] <- intermediate[slot, a-1, hv]: a plain copy of one dense
+// K x V block, 16 bytes per lane, kRollbackPerThread vectors in flight.
+__global__ void __launch_bounds__(kRollbackThreads) rollback_kernel(const RollbackParams p) {
+    const int chunk = blockIdx.x % p.chunks;
+    const int rh = blockIdx.x / p.chunks;
+    const int hv = rh % p.HV;
+    const int row = rh / p.HV;
+    const int32_t idx = p.idx[row];
+    const int32_t a = p.accepted[row];
+    if (idx < 0 || a < 1 || a > p.int_tokens) return;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.inter) + idx * p.in_slot + static_cast<int64_t>(a - 1) * p.in_tok +
+        hv * p.in_head);
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.state) + idx * p.st_slot +
+                                          hv * p.st_head);
+    const int64_t base = static_cast<int64_t>(chunk) * kRollbackThreads * kRollbackPerThread +
+                         threadIdx.x;
+    uint4 v[kRollbackPerThread];
+#pragma unroll
+    for (int j = 0; j < kRollbackPerThread; ++j) {
+        const int64_t i = base + j * kRollbackThreads;
+        if (i < p.block16) v[j] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kRollbackPerThread; ++j) {
+        const int64_t i = base + j * kRollbackThreads;
+        if (i < p.block16) dst[i] = v[j];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_rollback(const RollbackParams& p, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.rows) * p.HV * p.chunks);
+    hipLaunchKernelGGL(rollback_kernel, grid, dim3(kRollbackThreads), 0, stream, p);
+    return hipGetLastError();
+}
 
 // ------------------------------------------------------------- dispatch ---
 

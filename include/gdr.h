@@ -187,6 +187,27 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
                                const gdr_tensor* o, void* stream);
 
 /*
+ * gdr_snapshot_rollback - roll each request's cached state back to the
+ * snapshot taken after its last accepted draft token.
+ * Source: page "core.ssm.ops.gdp.fused_recurrent" (intermediate_states: entry
+ * [slot, i] holds the state after draft token i, so that verification can
+ * roll the recurrence back to any accepted prefix).
+ *
+ *   state               [S, HV, K, V] bf16|f32 cache (in/out)
+ *   state_indices       [N] i32|u32 cache slot per request, -1 = padding
+ *   intermediate_states [S, I, HV, K, V], same dtype as state (in)
+ *   accepted            [N] i32|u32 (device): accepted draft tokens a of
+ *                       request n
+ * For 1 <= a <= I: state[slot] <- intermediate_states[slot, a-1], a copy of
+ * the bits.  a == 0, a > I and padding requests leave the state untouched
+ * (the state before the first draft token is not among the snapshots; a
+ * caller that can accept zero drafts keeps its own copy).
+ */
+int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indices,
+                          const gdr_tensor* intermediate_states, const gdr_tensor* accepted,
+                          void* stream);
+
+/*
  * gdr_fwd_output_shape - shape of recurrence_output for the given conv
  * output and state pool: {qkv.shape[0], state.shape[1] * state.shape[3]}.
  * Source: page "gated_delta_recurrence_fwd_shape".  Host only; reads shapes

@@ -34,7 +34,8 @@ def _load():
             _build.build()
         _lib = ctypes.CDLL(_LIB_PATH)
         for name in ("oracle_recurrence_fwd", "oracle_recurrence_verify_ring",
-                     "oracle_state_fold", "oracle_fused_recurrent_update"):
+                     "oracle_state_fold", "oracle_fused_recurrent_update",
+                     "oracle_snapshot_rollback"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
 
@@ -51,7 +52,8 @@ class using_library:
         self.saved = _load()
         lib = ctypes.CDLL(self.path)
         for name in ("oracle_recurrence_fwd", "oracle_recurrence_verify_ring",
-                     "oracle_state_fold", "oracle_fused_recurrent_update"):
+                     "oracle_state_fold", "oracle_fused_recurrent_update",
+                     "oracle_snapshot_rollback"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -215,6 +217,27 @@ def fused_recurrent_update(*, q, k, v, g=None, beta=None, scale=None, initial_st
     if rc != 0:
         raise ValueError(f"oracle_fused_recurrent_update failed: {rc}")
     return o, (st if st is not None else final), inter
+
+
+def snapshot_rollback(*, state, state_indices, intermediate_states, accepted):
+    """Roll each request's state back to its snapshot after `accepted` draft
+    tokens ("core.ssm.ops.gdp.fused_recurrent", intermediate_states).
+
+    Returns the updated state copy."""
+    lib = _load()
+    st, bf = _state_copy(state)
+    inter = np.ascontiguousarray(intermediate_states)
+    if inter.dtype != st.dtype:
+        raise TypeError("state and intermediate_states must share a dtype")
+    idx = np.ascontiguousarray(state_indices, dtype=np.int32)
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    S, HV, K, V = st.shape
+    rc = lib.oracle_snapshot_rollback(
+        idx.shape[0], HV, K, V, st.itemsize, _p(st), ctypes.c_int64(S), _p(inter),
+        ctypes.c_int64(inter.shape[1]), _p(idx), _p(acc))
+    if rc != 0:
+        raise ValueError(f"oracle_snapshot_rollback failed: {rc}")
+    return st
 
 
 def fwd_output_shape(qkv_shape, state_shape):

@@ -458,3 +458,35 @@ void oracle_fwd_output_shape(int64_t total_seq_len, int64_t nv, int64_t V, int64
     out[0] = total_seq_len;
     out[1] = nv * V;
 }
+
+/* ------------------------------------------------- snapshot rollback ------ */
+
+/*
+ * [gdp] intermediate_states: entry [slot, i] is the state after draft token i,
+ * "so verification can roll the recurrence back to any accepted prefix".
+ * For request n with slot idx = state_indices[n] (>= 0) and accepted[n] = a
+ * draft tokens, 1 <= a <= int_tokens: state[idx] <- intermediate[idx, a-1].
+ * a == 0, a > int_tokens and padding requests (-1) leave the state alone (the
+ * state before the first draft token is not among the snapshots).
+ * state [num_slots, HV, K, V], intermediate [num_slots, int_tokens, HV, K, V],
+ * both of one storage type (elem_size bytes per element).
+ */
+int oracle_snapshot_rollback(int N, int HV, int K, int V, int elem_size, void* state,
+                             int64_t num_slots, const void* intermediate, int64_t int_tokens,
+                             const int32_t* state_indices, const int32_t* accepted)
+{
+    const int64_t block = (int64_t)HV * K * V * elem_size;
+    for (int n = 0; n < N; ++n) {
+        const int32_t idx = state_indices[n];
+        const int32_t a = accepted[n];
+        if (idx < 0 || a < 1 || (int64_t)a > int_tokens)
+            continue;
+        if ((int64_t)idx >= num_slots)
+            return -2;
+        const char* src = (const char*)intermediate + ((int64_t)idx * int_tokens + (a - 1)) * block;
+        char* dst = (char*)state + (int64_t)idx * block;
+        for (int64_t b = 0; b < block; ++b)
+            dst[b] = src[b];
+    }
+    return 0;
+}

@@ -365,6 +365,39 @@ def pin_snapshots():
             assert np.array_equal(st[s], w["state"][s])
 
 
+def pin_snapshot_rollback():
+    """Rolling a request back to its snapshot after n accepted draft tokens
+    gives the state a run over the first n * steps_per_token steps stores;
+    n = 0, n past the buffer and padding requests leave the state alone."""
+    rng = _rng(26)
+    w = wl.gdp_inputs(rng, B=6, S_draft=3, M=2, H=2, HV=4, K=8, V=8, slots=9, pad_frac=0.2,
+                      state_sigma=0.2)
+    args = {k: w[k] for k in ("q", "k", "v", "g", "beta", "state", "state_indices",
+                              "intermediate_states", "steps_per_token",
+                              "use_qk_l2norm_in_kernel", "scale")}
+    _, st, inter = oracle.fused_recurrent_update(**args)
+    M = w["steps_per_token"]
+    idx = w["state_indices"]
+    acc = np.full(len(idx), 2, np.int32)
+    active = np.flatnonzero(idx >= 0)
+    acc[active] = np.resize(np.array([1, 2, 3, 0, 4], np.int32), len(active))
+    rolled = oracle.snapshot_rollback(state=st, state_indices=idx, intermediate_states=inter,
+                                      accepted=acc)
+    for b, i in enumerate(idx):
+        if i < 0:
+            continue
+        n = int(acc[b])
+        if 1 <= n <= 3:
+            sub = dict(args, q=w["q"][:, :n * M], k=w["k"][:, :n * M], v=w["v"][:, :n * M],
+                       g=w["g"][:, :n * M], beta=w["beta"][:, :n * M], intermediate_states=None)
+            _, st_n, _ = oracle.fused_recurrent_update(**sub)
+            assert np.array_equal(rolled[i], st_n[i]), (b, n)
+        else:
+            assert np.array_equal(rolled[i], st[i]), (b, n)
+    others = np.setdiff1d(np.arange(9), idx[idx >= 0])
+    assert np.array_equal(rolled[others], st[others])
+
+
 def pin_golden_hand():
     """tests/golden/hand_k2_v2.json: a two-token example worked by hand in exact
     dyadic arithmetic."""
@@ -401,4 +434,4 @@ def pin_bf16_rounding():
 ALL_PINS = [pin_dense_fp64, pin_dense_unrolled, pin_beta_zero_decay_only, pin_delta_retrieval,
             pin_scalar_state, pin_gather_probe, pin_scatter_probe, pin_linearity_pow2,
             pin_verify_fold_identities, pin_replicated_heads, pin_fused_matches_packed,
-            pin_snapshots, pin_golden_hand, pin_bf16_rounding]
+            pin_snapshots, pin_snapshot_rollback, pin_golden_hand, pin_bf16_rounding]

@@ -154,3 +154,19 @@ def test_output_shape_helper():
     rc = L.gdr_fwd_output_shape(ctypes.byref(T([37, 8192])),
                                 ctypes.byref(T([512, 32, 128, 128], B.GDR_DTYPE_BF16)), out)
     assert rc == 0 and (out[0], out[1]) == (37, 4096)
+
+
+def test_rollback_argument_checks():
+    L = B.lib()
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+    st = T([6, 4, 16, 16], B.GDR_DTYPE_BF16)
+    inter = T([6, 3, 4, 16, 16], B.GDR_DTYPE_BF16)
+    idx = T([5], B.GDR_DTYPE_I32)
+    acc = T([5], B.GDR_DTYPE_I32)
+    assert L.gdr_snapshot_rollback(r(st), r(idx), r(T([6, 3, 4, 16, 16])), r(acc), None) == -2
+    assert L.gdr_snapshot_rollback(r(st), r(idx), r(T([7, 3, 4, 16, 16], B.GDR_DTYPE_BF16)),
+                                   r(acc), None) == -1
+    assert L.gdr_snapshot_rollback(r(st), r(idx), r(inter), r(T([4], B.GDR_DTYPE_I32)),
+                                   None) == -1
+    assert L.gdr_snapshot_rollback(r(st), r(T([0], B.GDR_DTYPE_I32)), r(inter),
+                                   r(T([0], B.GDR_DTYPE_I32)), None) == 0

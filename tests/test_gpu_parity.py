@@ -422,3 +422,38 @@ def test_fused_dense_and_varlen_paths():
     H.assert_close(o_g, o_r, "varlen output")
     H.assert_close(st_g, st_r, "varlen state")
     assert not o_g[0, 4:11].any()
+
+
+def test_snapshot_rollback_gpu():
+    """Rollback after n accepted drafts == a GPU run over the first n * spt
+    steps (bit for bit), and == the oracle's copy on the same arrays; n = 0,
+    n past the buffer and padding leave the state alone."""
+    import torch
+    import gated_delta_rule_loop_amd as gdr
+    rng = np.random.Generator(np.random.PCG64(78))
+    w = wl.gdp_inputs(rng, B=10, S_draft=3, M=2, H=4, HV=8, K=128, V=128, slots=14,
+                      pad_frac=0.2, state_sigma=0.05)
+    say("snapshot rollback, B=10 T=6 spt=2")
+    _, st, inter = H.gpu_fused(w)
+    idx = w["state_indices"]
+    acc = np.full(len(idx), 2, np.int32)
+    active = np.flatnonzero(idx >= 0)
+    acc[active] = np.resize(np.array([1, 2, 3, 0, 4], np.int32), len(active))
+    st_t = H.dev(st)
+    gdr.gdr_snapshot_rollback(st_t, H.dev(idx.astype(np.int32)), H.dev(inter), H.dev(acc))
+    torch.cuda.synchronize()
+    rolled = H.host(st_t)
+    want = oracle.snapshot_rollback(state=st, state_indices=idx, intermediate_states=inter,
+                                    accepted=acc)
+    assert np.array_equal(rolled, want)
+    M = w["steps_per_token"]
+    for b, i in enumerate(idx):
+        n = int(acc[b])
+        if i < 0 or not 1 <= n <= 3:
+            if i >= 0:
+                assert np.array_equal(rolled[i], st[i])
+            continue
+        sub = dict(w, q=w["q"][:, :n * M], k=w["k"][:, :n * M], v=w["v"][:, :n * M],
+                   g=w["g"][:, :n * M], beta=w["beta"][:, :n * M], intermediate_states=None)
+        _, st_n, _ = H.gpu_fused(sub)
+        assert np.array_equal(rolled[i], st_n[i]), (b, n)

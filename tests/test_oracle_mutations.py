@@ -32,6 +32,8 @@ MUTATIONS = [
      "const int64_t i = step / steps_per_token;"),
     ("padding_not_zero", "o[(f * HV + hv) * V + j] = 0.0f;", "o[(f * HV + hv) * V + j] = 1.0f;"),
     ("long_row_not_committed", "if (t1 > t0 && !use_ring)", "if (t1 > t0 && ring == NULL)"),
+    ("rollback_off_by_one", "((int64_t)idx * int_tokens + (a - 1)) * block",
+     "((int64_t)idx * int_tokens + a - (a > 1)) * block"),
     ("offsets_shifted", "const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];",
      "const int64_t t0 = row_offsets[b] + (b > 0), t1 = row_offsets[b + 1];"),
 ]
