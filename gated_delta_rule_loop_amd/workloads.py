@@ -124,17 +124,19 @@ def verify_window(seed: int = 1003, batch: int = 64, max_window: int = 12, ring_
 
 
 def gdp_inputs(rng, B, S_draft, M, H, HV, K, V, slots, pad_frac, state_sigma,
-               state_dtype="bf16"):
+               state_dtype="bf16", beta_per_v=False):
     """Gated DeltaProduct decode folded into the fused update: each of the
     S_draft draft tokens becomes M Householder copies; the query sits on the
     last copy (zero elsewhere) and the decay on the first (g = 0, i.e. a = 1,
-    elsewhere).  Returns the fused-update inputs with steps_per_token = M."""
+    elsewhere).  beta_per_v draws one beta per value column ([B, T, HV, V]).
+    Returns the fused-update inputs with steps_per_token = M."""
     T = S_draft * M
     q = rng.standard_normal((B, T, H, K)).astype(np.float32)
     k = rng.standard_normal((B, T, H, K)).astype(np.float32)
     v = rng.standard_normal((B, T, HV, V)).astype(np.float32)
     g = (-_softplus(rng.standard_normal((B, T, HV)))).astype(np.float32)
-    beta = _sigmoid(rng.standard_normal((B, T, HV))).astype(np.float32)
+    beta_shape = (B, T, HV, V) if beta_per_v else (B, T, HV)
+    beta = _sigmoid(rng.standard_normal(beta_shape)).astype(np.float32)
     copy = np.arange(T) % M
     q[:, copy != M - 1] = 0.0
     g[:, copy != 0] = 0.0

@@ -131,7 +131,8 @@ def recurrence_verify_ring(*, qkv, decay, beta, state, slot_idx, row_offsets, nu
                            num_key_heads, ring, ring_slot_idx, scale=None, l2norm=True):
     """Verify window with ring ("gated_delta_recurrence_verify_ring_gpu").
 
-    ring: float32 [ring_rows, nk, ring_len, rec_stride], copied.
+    ring: [ring_rows, nk, ring_len, rec_stride], float32 or uint16 (bf16 bits),
+    copied.
     Returns (out, state_after, ring_after)."""
     lib = _load()
     st, bf = _state_copy(state)
@@ -140,14 +141,15 @@ def recurrence_verify_ring(*, qkv, decay, beta, state, slot_idx, row_offsets, nu
     off = np.ascontiguousarray(row_offsets, dtype=np.uint32)
     sl = np.ascontiguousarray(slot_idx, dtype=np.uint32)
     rsl = np.ascontiguousarray(ring_slot_idx, dtype=np.uint32)
-    rg = np.array(ring, dtype=np.float32, order="C", copy=True)
+    rg, rbf = _state_copy(ring)
     B, T = sl.shape[0], qkv.shape[0]
     out = np.zeros((T, num_value_heads * V), dtype=np.float32)
     sc = default_scale(K) if scale is None else scale
     rc = lib.oracle_recurrence_verify_ring(
         B, num_value_heads, num_key_heads, K, V, _p(off), _p(sl), _p(qkv), _p(decay), _p(beta),
         bf, _p(st), ctypes.c_int64(st.shape[0]), _p(out), ctypes.c_float(sc), int(l2norm),
-        _p(rg), _p(rsl), ctypes.c_int64(rg.shape[0]), rg.shape[2], ctypes.c_int64(rg.shape[3]))
+        _p(rg), rbf, _p(rsl), ctypes.c_int64(rg.shape[0]), rg.shape[2],
+        ctypes.c_int64(rg.shape[3]))
     if rc != 0:
         raise ValueError(f"oracle_recurrence_verify_ring failed: {rc}")
     return out, st, rg
@@ -161,14 +163,17 @@ def state_fold(*, state, slot_idx, ring, ring_slot_idx, accepted, num_value_head
     lib = _load()
     st, bf = _state_copy(state)
     K, V = st.shape[2], st.shape[3]
-    rg = np.ascontiguousarray(ring, dtype=np.float32)
+    rg = np.ascontiguousarray(ring)
+    if rg.dtype not in (np.float32, np.uint16):
+        raise TypeError("ring must be float32 or uint16 (bf16 bits)")
+    rbf = int(rg.dtype == np.uint16)
     sl = np.ascontiguousarray(slot_idx, dtype=np.uint32)
     rsl = np.ascontiguousarray(ring_slot_idx, dtype=np.uint32)
     acc = np.ascontiguousarray(accepted, dtype=np.uint32)
     rc = lib.oracle_state_fold(
         sl.shape[0], num_value_heads, num_key_heads, K, V, _p(sl), bf, _p(st),
-        ctypes.c_int64(st.shape[0]), _p(rg), _p(rsl), ctypes.c_int64(rg.shape[0]), rg.shape[2],
-        ctypes.c_int64(rg.shape[3]), _p(acc))
+        ctypes.c_int64(st.shape[0]), _p(rg), rbf, _p(rsl), ctypes.c_int64(rg.shape[0]),
+        rg.shape[2], ctypes.c_int64(rg.shape[3]), _p(acc))
     if rc != 0:
         raise ValueError(f"oracle_state_fold failed: {rc}")
     return st

@@ -107,6 +107,21 @@ static void oracle_store_block(void* base, int bf16, int64_t offset, int64_t n, 
     }
 }
 
+/* One ring element, stored as float32 or rounded to bfloat16 ([verify]
+ * Parameters, ring_dtype). */
+static void oracle_ring_put(void* ring, int ring_bf16, int64_t i, float v)
+{
+    if (ring_bf16)
+        ((uint16_t*)ring)[i] = oracle_bf16_round(v);
+    else
+        ((float*)ring)[i] = v;
+}
+
+static float oracle_ring_get(const void* ring, int ring_bf16, int64_t i)
+{
+    return ring_bf16 ? oracle_bf16_widen(((const uint16_t*)ring)[i]) : ((const float*)ring)[i];
+}
+
 /* ------------------------------------------------------------ one step --- */
 
 /* x_hat = x / sqrt(sum x^2 + eps), written as a multiply by the reciprocal
@@ -199,7 +214,7 @@ static void oracle_packed_qk(const float* row, int nk, int K, int h, int l2norm,
 static int oracle_walk(int B, int nv, int nk, int K, int V, const uint32_t* row_offsets,
                        const uint32_t* slot_idx, const float* qkv, const float* decay,
                        const float* beta, int state_bf16, void* state, int64_t max_slots,
-                       float* out, float scale, int l2norm, float* ring,
+                       float* out, float scale, int l2norm, void* ring, int ring_bf16,
                        const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
                        int64_t rec_stride)
 {
@@ -242,13 +257,13 @@ static int oracle_walk(int B, int nv, int nk, int K, int V, const uint32_t* row_
                 oracle_step(K, V, S, khat, qhat, v, a, &bt, 0, scale,
                             out + t * nv * V + (int64_t)hv * V, u);
                 if (use_ring) {
-                    float* rec = ring + (((int64_t)rrow * nk + h) * ring_len + (t - t0)) * rec_stride;
+                    const int64_t rec = (((int64_t)rrow * nk + h) * ring_len + (t - t0)) * rec_stride;
                     if (m == 0)
                         for (int i = 0; i < K; ++i)
-                            rec[i] = khat[i];
+                            oracle_ring_put(ring, ring_bf16, rec + i, khat[i]);
                     for (int j = 0; j < V; ++j)
-                        rec[K + (int64_t)m * V + j] = u[j];
-                    rec[K + (int64_t)G * V + m] = a;
+                        oracle_ring_put(ring, ring_bf16, rec + K + (int64_t)m * V + j, u[j]);
+                    oracle_ring_put(ring, ring_bf16, rec + K + (int64_t)G * V + m, a);
                 }
             }
             if (t1 > t0 && !use_ring)
@@ -270,7 +285,7 @@ int oracle_recurrence_fwd(int B, int nv, int nk, int K, int V, const uint32_t* r
                           float* out, float scale, int l2norm)
 {
     return oracle_walk(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta, state_bf16,
-                       state, max_slots, out, scale, l2norm, NULL, NULL, 0, 0, 0);
+                       state, max_slots, out, scale, l2norm, NULL, 0, NULL, 0, 0, 0);
 }
 
 /* [verify]: the forward over a verify window, recording a float32 ring. */
@@ -278,22 +293,23 @@ int oracle_recurrence_verify_ring(int B, int nv, int nk, int K, int V,
                                   const uint32_t* row_offsets, const uint32_t* slot_idx,
                                   const float* qkv, const float* decay, const float* beta,
                                   int state_bf16, void* state, int64_t max_slots, float* out,
-                                  float scale, int l2norm, float* ring,
+                                  float scale, int l2norm, void* ring, int ring_bf16,
                                   const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
                                   int64_t rec_stride)
 {
     if (rec_stride < (int64_t)K + (int64_t)(nv / (nk > 0 ? nk : 1)) * (V + 1))
         return -1;
     return oracle_walk(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta, state_bf16,
-                       state, max_slots, out, scale, l2norm, ring, ring_slot_idx, ring_rows,
-                       ring_len, rec_stride);
+                       state, max_slots, out, scale, l2norm, ring, ring_bf16, ring_slot_idx,
+                       ring_rows, ring_len, rec_stride);
 }
 
 /* [verify] (fold paragraphs): advance the live state of row b over its first
  * accepted[b] ring records.  A count above ring_len (a row that committed in
  * full during verify) or of zero leaves the state alone. */
 int oracle_state_fold(int B, int nv, int nk, int K, int V, const uint32_t* slot_idx,
-                      int state_bf16, void* state, int64_t max_slots, const float* ring,
+                      int state_bf16, void* state, int64_t max_slots, const void* ring,
+                      int ring_bf16,
                       const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
                       int64_t rec_stride, const uint32_t* accepted)
 {
@@ -316,17 +332,19 @@ int oracle_state_fold(int B, int nv, int nk, int K, int V, const uint32_t* slot_
             const int64_t soff = ((int64_t)slot * nv + hv) * kv;
             oracle_load_block(state, state_bf16, soff, kv, S);
             for (uint32_t t = 0; t < n; ++t) {
-                const float* rec =
-                    ring + (((int64_t)ring_slot_idx[b] * nk + h) * ring_len + t) * rec_stride;
-                const float* khat = rec;
-                const float* u = rec + K + (int64_t)m * V;
-                const float a = rec[K + (int64_t)G * V + m];
+                const int64_t rec =
+                    (((int64_t)ring_slot_idx[b] * nk + h) * ring_len + t) * rec_stride;
+                const float a = oracle_ring_get(ring, ring_bf16, rec + K + (int64_t)G * V + m);
                 for (int i = 0; i < K; ++i)
                     for (int j = 0; j < V; ++j)
                         S[i * V + j] = a * S[i * V + j];
-                for (int i = 0; i < K; ++i)
-                    for (int j = 0; j < V; ++j)
-                        S[i * V + j] = S[i * V + j] + khat[i] * u[j];
+                for (int i = 0; i < K; ++i) {
+                    const float khat = oracle_ring_get(ring, ring_bf16, rec + i);
+                    for (int j = 0; j < V; ++j) {
+                        const float u = oracle_ring_get(ring, ring_bf16, rec + K + (int64_t)m * V + j);
+                        S[i * V + j] = S[i * V + j] + khat * u;
+                    }
+                }
             }
             oracle_store_block(state, state_bf16, soff, kv, S);
         }

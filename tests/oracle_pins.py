@@ -398,6 +398,70 @@ def pin_snapshot_rollback():
     assert np.array_equal(rolled[others], st[others])
 
 
+def pin_per_v_beta():
+    """Fused-update page, beta of shape [B, T, HV, V]: each value column j has
+    its own transition a (I - beta_j k k^T), checked against the fp64 matrix
+    form column by column; a per-column beta whose columns are all equal is
+    the head-wise beta, bit for bit."""
+    rng = _rng(27)
+    w = wl.gdp_inputs(rng, B=3, S_draft=3, M=2, H=2, HV=4, K=8, V=6, slots=5, pad_frac=0.0,
+                      state_sigma=0.3, state_dtype="f32", beta_per_v=True)
+    args = {k: w[k] for k in ("q", "k", "v", "g", "beta", "state", "state_indices",
+                              "use_qk_l2norm_in_kernel", "scale")}
+    o, st, _ = oracle.fused_recurrent_update(**args)
+    G = 4 // 2
+    for b, idx in enumerate(w["state_indices"]):
+        for hv in range(4):
+            h = hv // G
+            o_ref, S_ref = dense_ref.dense_walk(
+                w["state"][idx, hv], w["q"][b, :, h], w["k"][b, :, h], w["v"][b, :, hv],
+                np.exp(w["g"][b, :, hv].astype(np.float64)), w["beta"][b, :, hv], w["scale"],
+                True)
+            _close(o[b, :, hv], o_ref, 1e-5, f"o b{b} hv{hv}")
+            _close(st[idx, hv], S_ref, 1e-5, f"S b{b} hv{hv}")
+    head = w["beta"][..., 0]
+    flat = np.ascontiguousarray(np.repeat(head[..., None], 6, axis=-1))
+    o1, st1, _ = oracle.fused_recurrent_update(**dict(args, beta=head))
+    o2, st2, _ = oracle.fused_recurrent_update(**dict(args, beta=flat))
+    assert np.array_equal(o1, o2)
+    assert np.array_equal(st1, st2)
+
+
+def pin_bf16_ring():
+    """Verify page, ring_dtype bfloat16: every ring element is the float32
+    record rounded to bf16 once; folding a bf16 ring equals folding a float32
+    ring that holds the widened values, bit for bit; and it lands within the
+    bf16 rounding of the records from the forward over the accepted prefix."""
+    ring_len = 4
+    lengths = [2, 4, 3, 6]
+    nk, nv, K, V = 2, 4, 8, 8
+    w = small_packed(28, lengths, nk=nk, nv=nv, K=K, V=V, slots=6, state_dtype="f32")
+    stride = wl.ring_record_stride(nv // nk, K, V, align=8)
+    rslot = np.array([3, 0, 2, 1], np.uint32)
+    base = {k: w[k] for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets",
+                              "num_value_heads", "num_key_heads")}
+    ring_f = np.zeros((4, nk, ring_len, stride), np.float32)
+    ring_b = np.zeros((4, nk, ring_len, stride), np.uint16)
+    out_f, st_f, rf = oracle.recurrence_verify_ring(**base, ring=ring_f, ring_slot_idx=rslot)
+    out_b, st_b, rb = oracle.recurrence_verify_ring(**base, ring=ring_b, ring_slot_idx=rslot)
+    assert np.array_equal(out_f, out_b)
+    assert np.array_equal(st_f, st_b)
+    assert np.array_equal(rb, oracle.bf16_round(rf))
+    acc = np.array([1, 4, 3, 6], np.uint32)
+    fold = dict(slot_idx=w["slot_idx"], ring_slot_idx=rslot, accepted=acc, num_value_heads=nv,
+                num_key_heads=nk)
+    s_b = oracle.state_fold(state=st_b, ring=rb, **fold)
+    s_w = oracle.state_fold(state=st_b, ring=np.ascontiguousarray(wl.bf16_bits_to_f32(rb)),
+                            **fold)
+    assert np.array_equal(s_b, s_w)
+    s_f = oracle.state_fold(state=st_f, ring=rf, **fold)
+    for b in range(3):
+        s = w["slot_idx"][b]
+        _close(s_b[s], s_f[s], 2e-2, f"bf16 ring fold row {b}")
+        assert not np.array_equal(s_b[s], s_f[s])
+    assert np.array_equal(s_b[w["slot_idx"][3]], st_f[w["slot_idx"][3]])
+
+
 def pin_golden_hand():
     """tests/golden/hand_k2_v2.json: a two-token example worked by hand in exact
     dyadic arithmetic."""
@@ -434,4 +498,5 @@ def pin_bf16_rounding():
 ALL_PINS = [pin_dense_fp64, pin_dense_unrolled, pin_beta_zero_decay_only, pin_delta_retrieval,
             pin_scalar_state, pin_gather_probe, pin_scatter_probe, pin_linearity_pow2,
             pin_verify_fold_identities, pin_replicated_heads, pin_fused_matches_packed,
-            pin_snapshots, pin_snapshot_rollback, pin_golden_hand, pin_bf16_rounding]
+            pin_snapshots, pin_snapshot_rollback, pin_per_v_beta, pin_bf16_ring, pin_golden_hand,
+            pin_bf16_rounding]

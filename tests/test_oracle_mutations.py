@@ -26,14 +26,17 @@ MUTATIONS = [
     ("norm_no_sqrt", "float rho = 1.0f / sqrtf(sq + ORACLE_L2NORM_EPS);",
      "float rho = 1.0f / (sq + ORACLE_L2NORM_EPS);"),
     ("bf16_truncate", "x += 0x7fffu + keep_lsb;", "x += 0u * keep_lsb;"),
-    ("fold_wrong_head_a", "const float a = rec[K + (int64_t)G * V + m];",
-     "const float a = rec[K + (int64_t)G * V];"),
+    ("fold_wrong_head_a", "oracle_ring_get(ring, ring_bf16, rec + K + (int64_t)G * V + m);",
+     "oracle_ring_get(ring, ring_bf16, rec + K + (int64_t)G * V);"),
     ("snapshot_off_by_one", "const int64_t i = step / steps_per_token - 1;",
      "const int64_t i = step / steps_per_token;"),
     ("padding_not_zero", "o[(f * HV + hv) * V + j] = 0.0f;", "o[(f * HV + hv) * V + j] = 1.0f;"),
     ("long_row_not_committed", "if (t1 > t0 && !use_ring)", "if (t1 > t0 && ring == NULL)"),
     ("rollback_off_by_one", "((int64_t)idx * int_tokens + (a - 1)) * block",
      "((int64_t)idx * int_tokens + a - (a > 1)) * block"),
+    ("per_v_beta_ignored", "float b = beta_per_v ? beta[j] : beta[0];", "float b = beta[0];"),
+    ("ring_bf16_read_truncated", "return ring_bf16 ? oracle_bf16_widen(((const uint16_t*)ring)[i])",
+     "return ring_bf16 ? oracle_bf16_widen(((const uint16_t*)ring)[i] & 0xFF80u)"),
     ("offsets_shifted", "const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];",
      "const int64_t t0 = row_offsets[b] + (b > 0), t1 = row_offsets[b + 1];"),
 ]
