@@ -202,7 +202,7 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
 
     gdr::RecParams p{};
     if (ring) {
-        if ((rc = check_tensor(fn, "ring", ring, 4, nullptr, true, false, false))) return rc;
+        if ((rc = check_tensor(fn, "ring", ring, 4, nullptr, true, true, false))) return rc;
         if (ring->shape[1] != nk)
             return fail(GDR_ERR_INVALID_ARG, "%s: ring dim 1 must be num_key_heads", fn);
         if (ring->shape[2] < 1)
@@ -215,9 +215,11 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
                         static_cast<long long>(gdr_ring_record_elements(
                             static_cast<int32_t>(G), static_cast<int32_t>(K),
                             static_cast<int32_t>(V))));
-        if ((rc = check_layout(fn, "ring", ring, 4))) return rc;
+        if ((rc = check_layout(fn, "ring", ring, ring->dtype == GDR_DTYPE_BF16 ? 8 : 4)))
+            return rc;
         if ((rc = check_index_vec(fn, "ring_slot_idx", ring_slot_idx, B))) return rc;
-        p.ring = static_cast<float*>(ring->data);
+        p.ring = ring->data;
+        p.ring_bf16 = ring->dtype == GDR_DTYPE_BF16 ? 1 : 0;
         p.ring_idx = as_u32(ring_slot_idx);
         p.ring_row = ring->stride[0];
         p.ring_head = ring->stride[1];
@@ -324,7 +326,7 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
     if ((rc = check_index_vec(fn, "slot_idx", slot_idx, B))) return rc;
     if ((rc = check_index_vec(fn, "ring_slot_idx", ring_slot_idx, B))) return rc;
     if ((rc = check_index_vec(fn, "accepted", accepted, B))) return rc;
-    if ((rc = check_tensor(fn, "ring", ring, 4, nullptr, true, false, false))) return rc;
+    if ((rc = check_tensor(fn, "ring", ring, 4, nullptr, true, true, false))) return rc;
     const int64_t G = nv / nk;
     if (ring->shape[1] != nk)
         return fail(GDR_ERR_INVALID_ARG, "%s: ring dim 1 must be num_key_heads", fn);
@@ -333,7 +335,7 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
                                                   static_cast<int32_t>(K),
                                                   static_cast<int32_t>(V)))
         return fail(GDR_ERR_INVALID_ARG, "%s: ring record stride too small", fn);
-    if ((rc = check_layout(fn, "ring", ring, 4))) return rc;
+    if ((rc = check_layout(fn, "ring", ring, ring->dtype == GDR_DTYPE_BF16 ? 8 : 4))) return rc;
     if (B == 0) {
         g_last_error.clear();
         return GDR_OK;
@@ -350,7 +352,8 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
     p.state = recurrent_state->data;
     p.st_slot = recurrent_state->stride[0];
     p.st_head = recurrent_state->stride[1];
-    p.ring = static_cast<const float*>(ring->data);
+    p.ring = ring->data;
+    p.ring_bf16 = ring->dtype == GDR_DTYPE_BF16 ? 1 : 0;
     p.ring_idx = as_u32(ring_slot_idx);
     p.ring_row = ring->stride[0];
     p.ring_head = ring->stride[1];
@@ -391,9 +394,11 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
         return rc;
     const int64_t gshape[3] = {B, T, HV};
     if (present(g) && (rc = check_tensor(fn, "g", g, 3, gshape, true, false, false))) return rc;
-    if (present(beta)) {
-        if (beta->ndim == 4)
-            return fail(GDR_ERR_UNSUPPORTED, "%s: per-V-element beta is not built", fn);
+    const bool beta_cols = present(beta) && beta->ndim == 4;
+    if (beta_cols) {  // one beta per value column: [B, T, HV, V]
+        if ((rc = check_tensor(fn, "beta", beta, 4, v->shape, true, false, false))) return rc;
+        if ((rc = check_layout(fn, "beta", beta, 4))) return rc;
+    } else if (present(beta)) {
         if ((rc = check_tensor(fn, "beta", beta, 3, gshape, true, false, false))) return rc;
     }
     const int64_t oshape[4] = {B, T, HV, V};
@@ -490,6 +495,7 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     if (present(beta)) {
         p.beta = static_cast<const float*>(beta->data);
         p.b_seq = beta->stride[0]; p.b_tok = beta->stride[1]; p.b_head = beta->stride[2];
+        p.beta_cols = beta_cols ? 1 : 0;
     }
     p.out = static_cast<float*>(o->data);
     p.o_seq = o->stride[0]; p.o_tok = o->stride[1]; p.o_head = o->stride[2];

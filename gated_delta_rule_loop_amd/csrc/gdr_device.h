@@ -1,0 +1,666 @@
+// gfx950 (CDNA4) kernels of the gated delta rule recurrence.
+//
+// Method (pages "gated_delta_recurrence_fwd_gpu", summary; and
+// "core.ssm.ops.gdp.fused_recurrent", fused_recurrent_gated_delta_rule_fwd_kernel):
+// per (sequence, value head) a K x V float32 state is carried token by token:
+//     S <- a S;  u = beta (v - S^T k_hat);  S <- S + k_hat u^T;  o = scale S^T q_hat
+//
+// Work decomposition (ours, for 64-wide waves):
+//   * one wave owns the full K extent of BV = 8*CPL contiguous value columns of
+//     one value head: lane = 8*vl + kg holds key rows [kg*R, kg*R + R) (R = K/8)
+//     of columns [j0, j0 + CPL), j0 = 8*CPL*tile + CPL*vl.  The state stays in
+//     VGPRs for the whole row.
+//   * the K-reduction of every column (S^T k_hat and S^T q_hat) is an in-lane
+//     fused multiply-add chain over the R rows in ascending order followed by
+//     a butterfly over the 8 row groups, which are the 8 lanes of one DPP
+//     half-row (three DPP adds).  This order depends on K only, never on CPL,
+//     the chunk size or the workgroup shape, so every launch shape, the verify
+//     kernel and the fold produce identical bits.
+//   * a workgroup is WPG waves of one (row, key head); q/k of a chunk of C
+//     tokens are normalised once per workgroup and staged in LDS together with
+//     the chunk's v, decay and beta; the next chunk's global loads are issued
+//     before the current chunk is processed.
+//   * S^T k_hat of token t+1 is computed in the same register pass as the
+//     read-out S^T q_hat of token t, so only one pass over the state is made
+//     per token; decay is applied as r = a * (S^T k_hat) on the reduced value.
+//   * no MFMA: the token-serial recurrence is not a dense contraction.#pragma once
+
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+constexpr float kEps = 1e-6f;
+
+// ------------------------------------------------------------ cross-lane ---
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// x[lane] + x[lane ^ 16], bit-identical in both lanes of the pair.
+__device__ __forceinline__ float xor16_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// x[lane] + x[lane ^ 32], bit-identical in both lanes of the pair.
+__device__ __forceinline__ float xor32_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 8 key-row groups of a column, identical in all 8 lanes that
+// hold them.  Both lane layouts (row group in the low or in the high three
+// lane bits) add the groups as ((g0+g1)+(g2+g3)) + ((g4+g5)+(g6+g7)), so they
+// give identical bits.
+template <bool KG_LOW>
+__device__ __forceinline__ float sum_row_groups(float x) {
+    if constexpr (KG_LOW) {  // the 8 groups are the 8 lanes of one half-row
+        x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+        x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+        x = x + dpp<0x141>(x);  // row_half_mirror: quads are uniform, pairs quad 0/1
+    } else {                 // the groups are lanes l, l^8, ..., l^56
+        x = x + dpp<0x128>(x);  // row_ror:8 is lane ^ 8 inside a 16-lane row
+        x = xor16_sum(x);
+        x = xor32_sum(x);
+    }
+    return x;
+}
+
+// Sum over the whole wave, identical in every lane.
+__device__ __forceinline__ float sum_wave(float x) {
+    x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x = x + dpp<0x141>(x);  // row_half_mirror: quads are uniform, pairs quad 0/1
+    x = x + dpp<0x140>(x);  // row_mirror: half-rows are uniform, pairs them
+    x = xor16_sum(x);
+    x = xor32_sum(x);
+    return x;
+}
+
+// ------------------------------------------------------------- bf16 I/O ---
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int CPL>
+__device__ __forceinline__ void load_cols(const uint16_t* p, float* o) {
+    if constexpr (CPL == 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(p);
+        o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+        o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z); o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+    } else if constexpr (CPL == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+    } else if constexpr (CPL == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+        o[0] = bf16_lo(w); o[1] = bf16_hi(w);
+    } else {
+        o[0] = __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_cols(uint16_t* p, const float* s) {
+    if constexpr (CPL == 8) {
+        uint4 w;
+        w.x = pack_bf16x2(s[0], s[1]); w.y = pack_bf16x2(s[2], s[3]);
+        w.z = pack_bf16x2(s[4], s[5]); w.w = pack_bf16x2(s[6], s[7]);
+        *reinterpret_cast<uint4*>(p) = w;
+    } else if constexpr (CPL == 4) {
+        uint2 w;
+        w.x = pack_bf16x2(s[0], s[1]); w.y = pack_bf16x2(s[2], s[3]);
+        *reinterpret_cast<uint2*>(p) = w;
+    } else if constexpr (CPL == 2) {
+        *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(s[0], s[1]);
+    } else {
+        *p = static_cast<uint16_t>(pack_bf16x2(s[0], 0.0f) & 0xFFFFu);
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void load_cols(const float* p, float* o) {
+    if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; i += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(p + i);
+            o[i] = w.x; o[i + 1] = w.y; o[i + 2] = w.z; o[i + 3] = w.w;
+        }
+    } else if constexpr (CPL == 2) {
+        const float2 w = *reinterpret_cast<const float2*>(p);
+        o[0] = w.x; o[1] = w.y;
+    } else {
+        o[0] = *p;
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_cols(float* p, const float* s) {
+    if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; i += 4)
+            *reinterpret_cast<float4*>(p + i) = make_float4(s[i], s[i + 1], s[i + 2], s[i + 3]);
+    } else if constexpr (CPL == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(s[0], s[1]);
+    } else {
+        *p = s[0];
+    }
+}
+
+// ---------------------------------------------------- per-lane arithmetic ---
+
+// The state of one (row, value head) is held as scale * S: a token's decay
+// multiplies only the scalar (cn = scale * a), and the rank-1 write becomes
+// S += k_hat (u / cn)^T, one fused multiply-add per element.  When cn leaves
+// [2^-64, 2^64] (a zero decay included) the scale is folded into the registers
+// and reset to 1.  The forward, the verify and the fold run this same scalar
+// sequence from the same decays, so their states stay bit-identical.
+constexpr float kScaleLo = 5.421010862427522e-20f;  // 2^-64
+constexpr float kScaleHi = 1.8446744073709552e19f;  // 2^64
+
+template <int R, int CPL>
+__device__ __forceinline__ float decay_step(float (&S)[R][CPL], float cn) {
+    if (cn >= kScaleLo && cn <= kScaleHi) return cn;
+#pragma unroll
+    for (int ri = 0; ri < R; ++ri)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) S[ri][cc] = cn * S[ri][cc];
+    return 1.0f;
+}
+
+// out[c] = sum_ri S[ri][c] * vec[ri], ascending ri, fused multiply-adds.
+template <int R, int CPL>
+__device__ __forceinline__ void dot_rows(const float (&S)[R][CPL], const float (&vec)[R],
+                                         float (&out)[CPL]) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        float acc = S[0][c] * vec[0];
+#pragma unroll
+        for (int ri = 1; ri < R; ++ri) acc = __builtin_fmaf(S[ri][c], vec[ri], acc);
+        out[c] = acc;
+    }
+}
+
+// The R rows [kg*R, kg*R + R) of a K-vector staged in LDS with 4 floats of
+// padding after every R (so the 8 row groups hit different banks).
+template <int R>
+__device__ __forceinline__ void read_rows(const float* vec, int kg, float (&out)[R]) {
+    const float* src = vec + kg * (R + 4);
+    if constexpr (R % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < R; i += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(src + i);
+            out[i] = w.x; out[i + 1] = w.y; out[i + 2] = w.z; out[i + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) out[i] = src[i];
+    }
+}
+
+template <int R>
+__device__ __forceinline__ int pad_index(int i) { return i + (i / R) * 4; }
+
+// ------------------------------------------------------------- recurrence ---
+
+// Kernel modes: kPlain, kVerify or kSnap, plus the kBetaCols bit when beta
+// carries one value per value column.
+enum : int { kPlain = 0, kVerify = 1, kSnap = 2, kBetaCols = 4 };
+
+// One ring element: float32, or bf16 rounded to nearest even.
+__device__ __forceinline__ void ring_put(const RecParams& p, int64_t i, float x) {
+    if (p.ring_bf16)
+        store_cols<1>(static_cast<uint16_t*>(p.ring) + i, &x);
+    else
+        static_cast<float*>(p.ring)[i] = x;
+}
+
+// One work item: value columns [j0, j0 + CPL) of every key row, for one value
+// head of one row, resolved once per item.
+struct Item {
+    int row, h, part, m, vt, hv, j0, L;
+    int64_t rq, rk, rv, rg, rb, ro;
+    uint32_t slot;
+    bool pad, record;
+};
+
+template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW>
+struct Rec {
+    static constexpr int V = K;
+    static constexpr int R = K / kRowGroups;
+    static constexpr int BV = kLanesPerRow * CPL;
+    static constexpr int TILES = V / BV;
+    static constexpr int KP = K + 4 * kRowGroups;      // padded staged vector
+    static constexpr int QK = (K + 63) / 64;           // q/k elements per lane (norm)
+    static constexpr int SPW = (C + WPG - 1) / WPG;    // tokens normalised per wave
+    static constexpr int VTOT = C * BV;                // v floats per wave per chunk
+    static constexpr int VPL = VTOT >= 64 ? VTOT / 64 : 1;
+    static_assert(R >= 2 && TILES >= 1 && V % BV == 0, "tile shape");
+    static_assert(VTOT < 64 || VTOT % 64 == 0, "v staging");
+    static_assert(C <= 64, "gate staging uses one lane per token");
+
+    // LDS: two chunk buffers of [k_hat C x KP | q_hat*scale C x KP | v | a |
+    // beta | per-column beta (kBetaCols only)].
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_Q = C * KP;
+    static constexpr int OFF_V = 2 * C * KP;
+    static constexpr int OFF_A = OFF_V + WPG * VTOT;
+    static constexpr int OFF_B = OFF_A + WPG * C;
+    static constexpr int OFF_BV = (OFF_B + WPG * C + 3) / 4 * 4;
+    template <bool BC>
+    static constexpr int buf() { return BC ? OFF_BV + WPG * VTOT : OFF_BV; }
+
+    struct Stage {
+        float q[SPW][QK], k[SPW][QK], v[VPL], bv[VPL], a, b;
+    };
+
+    // Lane = 8 * column chunk + row group (KG_LOW) or 8 * row group + column
+    // chunk.  The first keeps each reduction inside a DPP half-row; the second
+    // keeps 8 consecutive lanes on one contiguous run of a state row.
+    __device__ static int row_group(int lane) { return KG_LOW ? (lane & 7) : (lane >> 3); }
+    __device__ static int col_chunk(int lane) { return KG_LOW ? (lane >> 3) : (lane & 7); }
+
+    __device__ static Item item(const RecParams& p, int idx, int w, int lane) {
+        Item it;
+        int blk = idx;
+        it.part = blk % p.parts;
+        blk /= p.parts;
+        it.h = blk % p.nk;
+        it.row = blk / p.nk;
+        const int unit = it.part * WPG + w;
+        it.m = unit / TILES;
+        it.vt = unit - it.m * TILES;
+        it.hv = it.h * p.G + it.m;
+        it.j0 = it.vt * BV + col_chunk(lane) * CPL;
+        if (p.offsets) {
+            const int64_t t0 = p.offsets[it.row];
+            it.L = static_cast<int>(static_cast<int64_t>(p.offsets[it.row + 1]) - t0);
+            it.rq = t0 * p.q_tok; it.rk = t0 * p.k_tok; it.rv = t0 * p.v_tok;
+            it.rg = t0 * p.g_tok; it.rb = t0 * p.b_tok; it.ro = t0 * p.o_tok;
+        } else {
+            const int64_t r = it.row;
+            it.L = p.dense_len;
+            it.rq = r * p.q_seq; it.rk = r * p.k_seq; it.rv = r * p.v_seq;
+            it.rg = r * p.g_seq; it.rb = r * p.b_seq; it.ro = r * p.o_seq;
+        }
+        it.slot = p.slot_idx ? p.slot_idx[it.row] : static_cast<uint32_t>(it.row);
+        it.pad = p.slot_idx != nullptr && it.slot == kPadSlot;
+        it.record = p.ring != nullptr && it.L <= p.ring_len;
+        return it;
+    }
+
+    __device__ static float* out_ptr(const RecParams& p, const Item& it) {
+        return p.out + it.ro + static_cast<int64_t>(it.hv) * p.o_head + it.j0;
+    }
+
+    __device__ static const ST* src_ptr(const RecParams& p, const Item& it) {
+        const int64_t sel = p.src_by_slot ? static_cast<int64_t>(it.slot) : it.row;
+        return static_cast<const ST*>(p.src) + sel * p.src_slot +
+               static_cast<int64_t>(it.hv) * p.src_head + it.j0;
+    }
+
+    // Padding request: +0.0 output for every token, nothing else.
+    __device__ static void zero_output(const RecParams& p, const Item& it, int lane) {
+        if (row_group(lane) != 0) return;
+        float z[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) z[c] = 0.0f;
+        float* outp = out_ptr(p, it);
+        for (int t = 0; t < it.L; ++t) store_cols<CPL>(outp + t * p.o_tok, z);
+    }
+
+    __device__ static void load_state(const RecParams& p, const Item& it, int kg,
+                                      float (&S)[R][CPL]) {
+        if (p.src) {
+            const ST* sp = src_ptr(p, it);
+#pragma unroll
+            for (int ri = 0; ri < R; ++ri) load_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
+        } else {
+#pragma unroll
+            for (int ri = 0; ri < R; ++ri)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) S[ri][c] = 0.0f;
+        }
+    }
+
+    // Stores the state scale * S.
+    __device__ static void store_tile(ST* base, int kg, float scale, const float (&S)[R][CPL]) {
+#pragma unroll
+        for (int ri = 0; ri < R; ++ri) {
+            float row[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) row[cc] = scale * S[ri][cc];
+            store_cols<CPL>(base + (kg * R + ri) * V, row);
+        }
+    }
+
+    __device__ static void store_state(const RecParams& p, const Item& it, int kg, float scale,
+                                       const float (&S)[R][CPL]) {
+        if (!p.dst || it.record) return;
+        const int64_t sel = p.dst_by_slot ? static_cast<int64_t>(it.slot) : it.row;
+        store_tile(static_cast<ST*>(p.dst) + sel * p.dst_slot +
+                       static_cast<int64_t>(it.hv) * p.dst_head + it.j0,
+                   kg, scale, S);
+    }
+
+    // v, or the per-column beta, of a chunk: VPL consecutive floats per lane
+    // of the wave's C x BV block.
+    __device__ static void load_block(const float* base, int64_t tok, int L, int tc, int lane,
+                                      float (&dst)[VPL]) {
+        const int flat = lane * VPL;
+        const int tau = flat / BV;
+        const int col = flat - tau * BV;
+        const int t = tc + tau;
+        const bool ok = flat < VTOT && t < L;
+        const float* vp = base + t * tok + col;
+        if constexpr (VPL == 4) {
+            float4 x = ok ? *reinterpret_cast<const float4*>(vp) : make_float4(0, 0, 0, 0);
+            dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
+        } else if constexpr (VPL == 2) {
+            float2 x = ok ? *reinterpret_cast<const float2*>(vp) : make_float2(0, 0);
+            dst[0] = x.x; dst[1] = x.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) dst[i] = ok ? vp[i] : 0.0f;
+        }
+    }
+
+    // Global loads of chunk c of an item into registers.
+    template <bool BC>
+    __device__ static void load_stage(const RecParams& p, const Item& it, int c, Stage& s,
+                                      int w, int lane) {
+        const int tc = c * C;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int tau = w + i * WPG;
+            const int t = tc + tau;
+            const bool ok = tau < C && t < it.L;
+#pragma unroll
+            for (int e = 0; e < QK; ++e) {
+                const int idx = lane + 64 * e;
+                const bool in = ok && idx < K;
+                s.q[i][e] = in ? p.q[it.rq + t * p.q_tok + it.h * p.q_head + idx] : 0.0f;
+                s.k[i][e] = in ? p.k[it.rk + t * p.k_tok + it.h * p.k_head + idx] : 0.0f;
+            }
+        }
+        load_block(p.v + it.rv + it.hv * p.v_head + it.vt * BV, p.v_tok, it.L, tc, lane, s.v);
+        if constexpr (BC)
+            load_block(p.beta + it.rb + it.hv * p.b_head + it.vt * BV, p.b_tok, it.L, tc, lane,
+                       s.bv);
+        {
+            const int t = tc + lane;
+            const bool ok = lane < C && t < it.L;
+            s.a = 1.0f;
+            s.b = 1.0f;
+            if (ok && p.gate) {
+                const float g = p.gate[it.rg + t * p.g_tok + it.hv * p.g_head];
+                s.a = p.gate_is_log ? expf(g) : g;
+            }
+            if (!BC && ok && p.beta) s.b = p.beta[it.rb + t * p.b_tok + it.hv * p.b_head];
+        }
+    }
+
+    // Norms of the staged tokens, then k_hat, q_hat*scale, v and gates to LDS.
+    // The first part of a (row, key head) also writes k_hat to the ring.
+    template <bool BC>
+    __device__ static void commit_stage(const RecParams& p, const Item& it, int c,
+                                        const Stage& s, float* B, int w, int lane) {
+        const int tc = c * C;
+        const int64_t rec = it.record ? static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
+                                            static_cast<int64_t>(it.h) * p.ring_head
+                                      : 0;
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int tau = w + i * WPG;
+            if (tau >= C) break;
+            float rk = 1.0f, rqs = p.scale;
+            if (p.l2norm) {
+                float kk = s.k[i][0] * s.k[i][0];
+                float qq = s.q[i][0] * s.q[i][0];
+#pragma unroll
+                for (int e = 1; e < QK; ++e) {
+                    kk = __builtin_fmaf(s.k[i][e], s.k[i][e], kk);
+                    qq = __builtin_fmaf(s.q[i][e], s.q[i][e], qq);
+                }
+                kk = sum_wave(kk);
+                qq = sum_wave(qq);
+                rk = rsqrtf(kk + kEps);
+                rqs = rsqrtf(qq + kEps) * p.scale;
+            }
+            const bool rec_k = it.record && it.part == 0 && tc + tau < it.L;
+#pragma unroll
+            for (int e = 0; e < QK; ++e) {
+                const int idx = lane + 64 * e;
+                if (idx < K) {
+                    const float kh = s.k[i][e] * rk;
+                    B[OFF_K + tau * KP + pad_index<R>(idx)] = kh;
+                    B[OFF_Q + tau * KP + pad_index<R>(idx)] = s.q[i][e] * rqs;
+                    if (rec_k) ring_put(p, rec + (tc + tau) * p.ring_tok + idx, kh);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int flat = lane * VPL + i;
+            if (flat < VTOT) B[OFF_V + w * VTOT + flat] = s.v[i];
+            if (BC && flat < VTOT) B[OFF_BV + w * VTOT + flat] = s.bv[i];
+        }
+        if (lane < C) {
+            B[OFF_A + w * C + lane] = s.a;
+            B[OFF_B + w * C + lane] = s.b;
+        }
+    }
+
+    // The tokens of chunk c, staged in B.  The state before the chunk is
+    // scale * S; both are updated (see decay_step for the representation).
+    // REC: record the ring for rows that fit it (verify); SNAP: store snapshots.
+    template <bool REC, bool SNAP, bool BC>
+    __device__ static void run_chunk(const RecParams& p, const Item& it, int c, const float* B,
+                                     float (&S)[R][CPL], float& scale, int w, int lane) {
+        const int kg = row_group(lane);
+        const int vc = col_chunk(lane) * CPL;
+        const int tc = c * C;
+        const int Lc = min(C, it.L - tc);
+        float* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
+        int64_t rec = 0;  // ring element offset of this token's record
+        if (REC && it.record)
+            rec = static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
+                  static_cast<int64_t>(it.h) * p.ring_head + static_cast<int64_t>(tc) * p.ring_tok;
+        ST* snap = nullptr;
+        int snap_left = 0;
+        if constexpr (SNAP) {  // steps until the next snapshot, and its entry
+            const int done = tc % p.spt;
+            snap_left = p.spt - done;
+            snap = static_cast<ST*>(p.snap) + static_cast<int64_t>(it.slot) * p.snap_slot +
+                   static_cast<int64_t>(tc / p.spt) * p.snap_tok +
+                   static_cast<int64_t>(it.hv) * p.snap_head + it.j0;
+        }
+        int snap_i = SNAP ? tc / p.spt : 0;
+
+        float kr[R];
+        read_rows<R>(B + OFF_K, kg, kr);
+        float x[CPL];  // S^T k_hat of the current token, before the scale
+        dot_rows<R, CPL>(S, kr, x);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
+
+        for (int tau = 0; tau < Lc; ++tau) {
+            const float a = B[OFF_A + w * C + tau];
+            float vv[CPL], be[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) vv[cc] = B[OFF_V + w * VTOT + tau * BV + vc + cc];
+            if constexpr (BC) {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) be[cc] = B[OFF_BV + w * VTOT + tau * BV + vc + cc];
+            } else {
+                const float b = B[OFF_B + w * C + tau];
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) be[cc] = b;
+            }
+            // r = S_{t-1}^T k_hat with this token's decay: (scale * a) * x
+            const float cn = scale * a;
+            float u[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) u[cc] = be[cc] * (vv[cc] - cn * x[cc]);
+            scale = decay_step<R, CPL>(S, cn);
+            const float rho = __builtin_amdgcn_rcpf(scale);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float us = u[cc] * rho;
+#pragma unroll
+                for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us, S[ri][cc]);
+            }
+
+            float qr[R];
+            read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
+            float o[CPL];
+            dot_rows<R, CPL>(S, qr, o);
+            if (C > 1 && tau + 1 < Lc) {
+                read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
+                dot_rows<R, CPL>(S, kr, x);
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
+            }
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups<KG_LOW>(o[cc]);
+
+            if (kg == 0) store_cols<CPL>(outp, o);
+            outp += p.o_tok;
+            if (REC && it.record) {
+                const int64_t ru = rec + K + it.m * V + it.j0;
+                if (kg == 0) {
+                    if (p.ring_bf16)
+                        store_cols<CPL>(static_cast<uint16_t*>(p.ring) + ru, u);
+                    else
+                        store_cols<CPL>(static_cast<float*>(p.ring) + ru, u);
+                }
+                if (it.vt == 0 && lane == 0) ring_put(p, rec + K + p.G * V + it.m, a);
+                rec += p.ring_tok;
+            }
+            if constexpr (SNAP) {
+                if (--snap_left == 0) {
+                    snap_left = p.spt;
+                    if (snap_i < p.snap_count) store_tile(snap, kg, scale, S);
+                    ++snap_i;
+                    snap += p.snap_tok;
+                }
+            }
+        }
+    }
+
+    // MODE: kPlain (forward, fused update without snapshots), kVerify (rows
+    // that fit the ring record it; longer rows run as kPlain), kSnap; with
+    // kBetaCols, beta is read per value column.
+    template <int MODE>
+    __device__ static void run_chunk_mode(const RecParams& p, const Item& it, int c,
+                                          const float* B, float (&S)[R][CPL], float& scale, int w,
+                                          int lane) {
+        run_chunk<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
+            p, it, c, B, S, scale, w, lane);
+    }
+
+    // All chunks of an item whose state is scale * S and whose chunk-0 inputs
+    // are in st.
+    template <int MODE>
+    __device__ static void run_item(const RecParams& p, const Item& it, float (&S)[R][CPL],
+                                    float& scale, Stage& st, float* lds, int w, int lane) {
+        constexpr bool BC = (MODE & kBetaCols) != 0;
+        constexpr int BUF = buf<BC>();
+        commit_stage<BC>(p, it, 0, st, lds, w, lane);
+        __syncthreads();
+        const int nch = (it.L + C - 1) / C;
+        for (int c = 0; c < nch; ++c) {
+            const bool next = c + 1 < nch;
+            if (next) load_stage<BC>(p, it, c + 1, st, w, lane);
+            run_chunk_mode<MODE>(p, it, c, lds + (c & 1) * BUF, S, scale, w, lane);
+            if (next) {
+                commit_stage<BC>(p, it, c + 1, st, lds + ((c + 1) & 1) * BUF, w, lane);
+                __syncthreads();
+            }
+        }
+    }
+};
+
+// One work item per workgroup.
+// One-token stages are the HBM-bound decode shape: ask for 4 waves per SIMD.
+template <int C>
+constexpr int kMinWaves = C == 1 ? 4 : 1;
+
+template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, int MODE>
+__global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecParams p) {
+    using Q = Rec<K, CPL, C, WPG, ST, KG_LOW>;
+    __shared__ __attribute__((aligned(16))) float lds[2 * Q::template buf<(MODE & kBetaCols) != 0>()];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int kg = Q::row_group(lane);
+    const Item it = Q::item(p, blockIdx.x, w, lane);
+    if (it.pad) {
+        Q::zero_output(p, it, lane);
+        return;
+    }
+    if (it.L <= 0) return;
+    float S[Q::R][CPL];
+    Q::load_state(p, it, kg, S);
+    float scale = 1.0f;
+    typename Q::Stage st;
+    Q::template load_stage<(MODE & kBetaCols) != 0>(p, it, 0, st, w, lane);
+    Q::template run_item<MODE>(p, it, S, scale, st, lds, w, lane);
+    Q::store_state(p, it, kg, scale, S);
+}
+
+}  // namespace
+
+template <int K, int CPL, int C, typename ST, bool KG_LOW, int MODE>
+static hipError_t launch_rec_mode(const RecParams& p, int wpg, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(p.rows) * p.nk * p.parts);
+    constexpr int TILES = K / (kLanesPerRow * CPL);
+    if constexpr (TILES % 4 == 0) {  // every head splits into a multiple of 4 waves
+        if (wpg != 4) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, MODE>), grid, dim3(256), 0, stream, p);
+    } else {
+        switch (wpg) {
+            case 1: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 1, ST, KG_LOW, MODE>), grid, dim3(64), 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 2, ST, KG_LOW, MODE>), grid, dim3(128), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, MODE>), grid, dim3(256), 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
+}
+
+// One (state type, mode) table of recurrence launch shapes.  Each table is
+// instantiated in a translation unit of its own (gdr_rec_table.hip), so the
+// library compiles in parallel.
+template <typename ST, int MODE>
+hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_t stream) {
+#define GDR_REC_CASE(KK, CC, CH, KL)                                              \
+    if (s.K == KK && s.cpl == CC && s.chunk == CH && s.kg_low == KL)             \
+        return launch_rec_mode<KK, CC, CH, ST, KL, MODE>(p, s.wpg, stream);
+    GDR_REC_CASE(128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
+    GDR_REC_CASE(128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
+    GDR_REC_CASE(128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
+    GDR_REC_CASE(128, GDR_LONG_CPL, GDR_LONG_CHUNK, GDR_LONG_KGLOW)
+#ifndef GDR_ONLY_K128
+    GDR_REC_CASE(64, 8, 8, false)
+    GDR_REC_CASE(64, 2, 16, true)
+    GDR_REC_CASE(32, 4, 8, false)
+    GDR_REC_CASE(32, 2, 16, true)
+    GDR_REC_CASE(16, 2, 8, false)
+    GDR_REC_CASE(16, 2, 16, true)
+#endif
+#undef GDR_REC_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

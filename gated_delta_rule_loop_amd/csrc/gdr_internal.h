@@ -25,6 +25,7 @@ struct RecParams {
     const float* gate; int64_t g_seq, g_tok, g_head;   // nullptr: a = 1
     int32_t gate_is_log;                               // a = exp(gate)
     const float* beta; int64_t b_seq, b_tok, b_head;   // nullptr: beta = 1
+    int32_t beta_cols;                                 // beta has a unit-stride V axis
     float* out; int64_t o_seq, o_tok, o_head;
 
     // State: slot = slot_idx[row] (nullptr: slot = row).  kPadSlot pads.
@@ -35,9 +36,10 @@ struct RecParams {
     // Snapshots (fused update): entry i after (i+1)*spt steps, at dst slot.
     void* snap; int64_t snap_slot, snap_tok, snap_head; int32_t snap_count, spt;
 
-    // Verify ring: rows with length <= ring_len record and do not store.
-    float* ring; const uint32_t* ring_idx;
-    int64_t ring_row, ring_head, ring_tok; int32_t ring_len;
+    // Verify ring (float32, or bf16 when ring_bf16): rows with length <=
+    // ring_len record and do not store.
+    void* ring; const uint32_t* ring_idx;
+    int64_t ring_row, ring_head, ring_tok; int32_t ring_len, ring_bf16;
 
     float scale;
     int32_t l2norm;
@@ -47,8 +49,8 @@ struct FoldParams {
     int32_t rows, nv, nk, G, parts;
     const uint32_t* slot_idx;
     void* state; int64_t st_slot, st_head;
-    const float* ring; const uint32_t* ring_idx;
-    int64_t ring_row, ring_head, ring_tok; int32_t ring_len;
+    const void* ring; const uint32_t* ring_idx;
+    int64_t ring_row, ring_head, ring_tok; int32_t ring_len, ring_bf16;
     const uint32_t* accepted;
 };
 

@@ -103,17 +103,19 @@ int gdr_recurrence_fwd(int32_t num_value_heads, int32_t num_key_heads,
  * ring_dtype and RING_LEN, Args ring / ring_slot_idx / ring_record_stride).
  *
  * Arguments as gdr_recurrence_fwd, plus
- *   ring              [ring_rows, nk, RING_LEN, record_stride] f32 (out); the
- *                     ring length is shape[2], record_stride is shape[3] and
- *                     must be >= gdr_ring_record_elements(nv/nk, K, V)
+ *   ring              [ring_rows, nk, RING_LEN, record_stride] f32|bf16 (out);
+ *                     the ring length is shape[2], record_stride is shape[3]
+ *                     and must be >= gdr_ring_record_elements(nv/nk, K, V);
+ *                     outer strides a multiple of 16 bytes
  *   ring_slot_idx     [B] u32|i32     ring row per batch row
  * Output equals gdr_recurrence_fwd's bit for bit.  A row of length
  * <= RING_LEN writes record [ring_row, key head, t] for each of its tokens t
  * and leaves recurrent_state untouched; a longer row writes no record and
  * stores its state exactly as the forward does (it commits in full).
  * Record layout (elements): [ k_hat (K) | u of value heads h*G+m, m < G (G*V)
- * | decay a of those heads (G) ] - the exact float32 operands of the state
- * update, so the fold needs no norm, exp or reduction.
+ * | decay a of those heads (G) ] - the float32 operands of the state update
+ * (rounded once to nearest-even bf16 in a bf16 ring), so the fold needs no
+ * norm, exp or reduction.
  */
 int gdr_recurrence_verify_ring(int32_t num_value_heads, int32_t num_key_heads,
                                const gdr_tensor* recurrence_output,
@@ -133,13 +135,15 @@ int gdr_recurrence_verify_ring(int32_t num_value_heads, int32_t num_key_heads,
  *
  *   recurrent_state   [slots, nv, K, V] bf16|f32 (in/out)
  *   slot_idx          [B] u32|i32
- *   ring              [ring_rows, nk, RING_LEN, record_stride] f32 (in)
+ *   ring              [ring_rows, nk, RING_LEN, record_stride] f32|bf16 (in)
  *   ring_slot_idx     [B] u32|i32
  *   accepted          [B] u32|i32 (device) accepted token count n of row b
  * n == 0 or n > RING_LEN leaves the row alone (a row longer than RING_LEN
  * already committed in verify: pass its full length).  Otherwise records
- * 0..n-1 are applied; the result equals gdr_recurrence_fwd over the first n
- * tokens bit for bit.
+ * 0..n-1 are applied.  With a float32 ring the result equals
+ * gdr_recurrence_fwd over the first n tokens bit for bit; a bf16 ring gives
+ * the fold of the widened records, which differs from it by the records'
+ * rounding.
  */
 int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
                    const gdr_tensor* recurrent_state, const gdr_tensor* slot_idx,
@@ -156,7 +160,8 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
  *   q, k              [B, T, H, K] f32
  *   v                 [B, T, HV, V] f32
  *   g                 [B, T, HV] f32 log decay (a = exp(g)), or absent (a = 1)
- *   beta              [B, T, HV] f32, or absent (beta = 1)
+ *   beta              [B, T, HV] f32, or [B, T, HV, V] f32 with unit stride
+ *                     over V (one beta per value column), or absent (beta = 1)
  *   scale             <= 0 or NaN selects K^-0.5
  *   initial_state     [N, HV, K, V] bf16|f32 or absent (zeros); ignored when
  *                     state is given

@@ -119,6 +119,16 @@ def test_verify_requires_a_ring_with_room():
                                       r(a["qkv"]), r(a["decay"]), r(a["beta"]), r(a["off"]),
                                       None, None, ctypes.c_float(-1), 1, None)
     assert rc == -1
+    # a bf16 ring needs 16-byte outer strides (multiples of 8 elements)
+    odd = T([8, 2, 4, 52], B.GDR_DTYPE_BF16)
+    rc = L.gdr_recurrence_verify_ring(4, 2, r(a["out"]), r(a["state"]), r(a["slot"]),
+                                      r(a["qkv"]), r(a["decay"]), r(a["beta"]), r(a["off"]),
+                                      r(odd), r(T([4], B.GDR_DTYPE_U32)), ctypes.c_float(-1), 1,
+                                      None)
+    assert rc == -2 and "multiple of 8" in B.gdr_last_error_message()
+    rc = L.gdr_state_fold(4, 2, r(a["state"]), r(a["slot"]), r(odd), r(T([4], B.GDR_DTYPE_U32)),
+                          r(T([4], B.GDR_DTYPE_U32)), None)
+    assert rc == -2
 
 
 def test_fused_argument_checks():
@@ -141,7 +151,8 @@ def test_fused_argument_checks():
     assert call(cu=T([3], B.GDR_DTYPE_I32)) == -1                  # varlen needs B == 1
     assert call(spt=0) == -1
     assert call(inter=T([4, 3, 4, 16, 16], B.GDR_DTYPE_BF16)) == -1  # snapshots need a state
-    assert call(beta=T([2, 3, 4, 16])) == -2                       # per-V beta not built
+    assert call(beta=T([2, 3, 4, 8])) == -1                        # per-V beta must match v
+    assert call(beta=T([2, 3, 4, 16], stride=[192, 64, 1, 4])) == -2  # V axis not unit stride
     assert call(v=T([2, 3, 4, 32]), o=T([2, 3, 4, 32])) == -2      # K != V
     st = T([5, 4, 16, 16], B.GDR_DTYPE_BF16)
     assert call(state=st, inter=T([5, 3, 4, 16, 16], B.GDR_DTYPE_F32)) == -2  # dtype mismatch

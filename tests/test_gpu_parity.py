@@ -457,3 +457,90 @@ def test_snapshot_rollback_gpu():
                    g=w["g"][:, :n * M], beta=w["beta"][:, :n * M], intermediate_states=None)
         _, st_n, _ = H.gpu_fused(sub)
         assert np.array_equal(rolled[i], st_n[i]), (b, n)
+
+
+# ------------------------------------------- per-column beta, bf16 ring ---
+
+@pytest.mark.parametrize("case", [
+    # (B, S_draft, M, H, HV, K, state dtype, snapshots): fused short rows,
+    # decode (one step), long rows, and the smaller head dims
+    (16, 4, 2, 4, 8, 128, "bf16", True),
+    (24, 1, 1, 4, 8, 128, "bf16", False),
+    (3, 20, 2, 2, 4, 128, "f32", True),
+    (5, 3, 2, 2, 4, 64, "f32", True),
+    (4, 6, 1, 2, 8, 32, "bf16", False),
+    (6, 2, 3, 1, 2, 16, "f32", True),
+], ids=lambda c: "B{}_S{}_M{}_H{}_HV{}_K{}_{}_{}".format(*c[:7], "snap" if c[7] else "nosnap"))
+def test_per_column_beta_gpu(case):
+    """Fused update with beta [B, T, HV, V] against the oracle; a per-column
+    beta whose columns are equal gives the head-wise result bit for bit."""
+    B, S, M, Hh, HV, K, sd, snap = case
+    rng = np.random.Generator(np.random.PCG64(90 + K + B))
+    w = wl.gdp_inputs(rng, B=B, S_draft=S, M=M, H=Hh, HV=HV, K=K, V=K, slots=B + 3,
+                      pad_frac=0.15, state_sigma=0.1, state_dtype=sd, beta_per_v=True)
+    if not snap:
+        w["intermediate_states"] = None
+    say(f"per-column beta: {case}")
+    o_g, st_g, inter_g = H.gpu_fused(w)
+    o_r, st_r, inter_r = fused_oracle(w)
+    st_u = inter_u = None  # unrounded oracle states, to judge bf16 rounding ties
+    if sd == "bf16" and snap:
+        _, st_u, inter_u = fused_oracle(w, f32=True)
+    elif sd == "bf16":
+        _, st_u, _ = oracle.fused_recurrent_update(**{**{k: w[k] for k in (
+            "q", "k", "v", "g", "beta", "state_indices", "steps_per_token",
+            "use_qk_l2norm_in_kernel", "scale")}, "state": H.f32_pool(w["state"])})
+    err = H.assert_close(o_g, o_r, "per-column beta output")
+    idx = w["state_indices"]
+    sl = idx[idx >= 0].astype(np.int64)
+    H.assert_state_close(st_g[sl], st_r[sl], "per-column beta state",
+                         None if st_u is None else st_u[sl])
+    if snap:
+        H.assert_state_close(inter_g[sl], inter_r[sl], "per-column beta snapshots",
+                             None if inter_u is None else inter_u[sl])
+    head = np.ascontiguousarray(w["beta"][..., 0])
+    flat = np.ascontiguousarray(np.repeat(head[..., None], K, axis=-1))
+    o1, st1, i1 = H.gpu_fused(w, beta=head)
+    o2, st2, i2 = H.gpu_fused(w, beta=flat)
+    bits = lambda a: a.view(np.uint32 if a.dtype == np.float32 else np.uint16)  # noqa: E731
+    assert np.array_equal(bits(o1), bits(o2))
+    assert np.array_equal(bits(st1), bits(st2))
+    if snap:  # untouched entries hold NaN sentinels: compare bits
+        assert np.array_equal(bits(i1), bits(i2))
+    say(f"per-column beta: out rel err {err:.2e}")
+
+
+def test_bf16_ring_verify_and_fold():
+    """Verify with a bf16 ring: output and state as with a float32 ring, bit
+    for bit; every record is the float32 record rounded to nearest even; the
+    fold of the bf16 ring equals the fold of its widened values bit for bit
+    and the oracle's bf16-ring fold within tolerance."""
+    import torch
+    w = wl.verify_window()
+    lens = np.diff(w["row_offsets"].astype(np.int64))
+    ring_len = w["ring"].shape[2]
+    ring_b0 = np.zeros(w["ring"].shape, np.uint16)
+    say("bf16 ring: verify window B=64, ring_len 8")
+    out_f, st_f, ring_f = H.gpu_verify(w)
+    out_b, st_b, ring_b = H.gpu_verify(w, ring=ring_b0)
+    assert np.array_equal(out_b.view(np.uint32), out_f.view(np.uint32))
+    assert np.array_equal(st_b, st_f)
+    want = torch.from_numpy(ring_f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ring_b, want), "bf16 ring != rounded float32 ring"
+    acc = w["accepted"]
+    fold_b = H.gpu_fold(w, st_b, ring_b, acc)
+    fold_w = H.gpu_fold(w, st_b, np.ascontiguousarray(wl.bf16_bits_to_f32(ring_b)), acc)
+    assert np.array_equal(fold_b, fold_w), "bf16-ring fold != fold of widened records"
+    args = {k: w[k] for k in ("qkv", "decay", "beta", "slot_idx", "row_offsets",
+                              "num_value_heads", "num_key_heads", "ring_slot_idx")}
+    _, st_r, ring_r = oracle.recurrence_verify_ring(**args, state=w["state"], ring=ring_b0)
+    _, unr_v, ring_ru = oracle.recurrence_verify_ring(**args, state=H.f32_pool(w["state"]),
+                                                      ring=ring_b0)
+    fold_kw = dict(slot_idx=w["slot_idx"], ring_slot_idx=w["ring_slot_idx"], accepted=acc,
+                   num_value_heads=32, num_key_heads=16)
+    fold_r = oracle.state_fold(state=st_r, ring=ring_r, **fold_kw)
+    unr_f = oracle.state_fold(state=unr_v, ring=ring_ru, **fold_kw)
+    sl = touched(w)
+    ties = H.assert_state_close(fold_b[sl], fold_r[sl], "bf16-ring fold state", unr_f[sl])
+    n_fit = int((lens <= ring_len).sum())
+    say(f"bf16 ring: {n_fit} rows folded, fold ties {ties}")
