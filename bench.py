@@ -1,6 +1,7 @@
 """Benchmark of the gated delta rule recurrence on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,verify,gdp]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--only decode,decode_bf16,prefill,verify,gdp]
                     [--no-cpu-baseline] [--copy-probe MiB]
 
 Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
@@ -11,9 +12,10 @@ launches touch disjoint memory (R * 512 MiB of pool, well above the 256 MB
 Infinity Cache).  The per-launch time is the HIP-event time of the timed
 region on the stream the kernels run on, divided by the launch count.
 
-Also timed (reported under "configs"): the ragged prefill (VALU-bound), the
-speculative verify + fold (HBM-bound) and the Gated DeltaProduct decode with
-snapshots (HBM-bound).  The CPU baseline is the plain C oracle timed on the
+Also timed (reported under "configs"): the decode step with bf16 per-token
+inputs and output, the ragged prefill (VALU-bound), the speculative verify +
+fold (HBM-bound) and the Gated DeltaProduct decode with snapshots and the
+snapshot rollback (HBM-bound).  The CPU baseline is the plain C oracle timed on the
 host on a bounded sample of the decode workload.
 """
 from __future__ import annotations
@@ -92,7 +94,8 @@ def _packed_launch(torch, gdr, B, w, ring=False, stream=None):
                                        "row_offsets")}
     T = w["qkv"].shape[0]
     V = w["state"].shape[3]
-    d["out"] = torch.empty((T, w["num_value_heads"] * V), dtype=torch.float32, device="cuda")
+    work = torch.bfloat16 if w["qkv"].dtype == np.uint16 else torch.float32
+    d["out"] = torch.empty((T, w["num_value_heads"] * V), dtype=work, device="cuda")
     keep = dict(d)
     L = B.lib()
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -129,6 +132,20 @@ def case_decode(torch, gdr, B, wl, rotations):
     alg = state + Bn * 8192 * 4 + Bn * nv * K * 4 + 2 * Bn * nv * 4 + (2 * Bn + 1) * 4
     flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
     return Case("decode_256x1", launches, alg, state, Bn, flops)
+
+
+def case_decode_bf16(torch, gdr, B, wl, rotations):
+    """The decode step with bf16 per-token inputs and output (work dtype)."""
+    launches = []
+    for r in range(rotations):
+        w = wl.bf16_work(wl.decode_step(seed=1001 + 100 * r))
+        launch, _ = _packed_launch(torch, gdr, B, w)
+        launches.append(launch)
+    Bn, nv, K = 256, 32, 128
+    state = Bn * nv * K * K * 2 * 2
+    alg = state + Bn * 8192 * 2 + Bn * nv * K * 2 + 2 * Bn * nv * 2 + (2 * Bn + 1) * 4
+    flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
+    return Case("decode_256x1_bf16io", launches, alg, state, Bn, flops)
 
 
 def case_prefill(torch, gdr, B, wl, rotations):
@@ -316,7 +333,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotations", type=int, default=4)
-    ap.add_argument("--only", default="decode,prefill,verify,gdp")
+    ap.add_argument("--only", default="decode,decode_bf16,prefill,verify,gdp")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -338,6 +355,8 @@ def main():
     cases = []
     if "decode" in only:
         cases.append(case_decode(torch, gdr, B, wl, args.rotations))
+    if "decode_bf16" in only:
+        cases.append(case_decode_bf16(torch, gdr, B, wl, args.rotations))
     if "prefill" in only:
         cases.append(case_prefill(torch, gdr, B, wl, 2))
     if "verify" in only:

@@ -161,10 +161,11 @@ def gdr_fused_recurrent_update(q, k, v, g=None, beta=None, scale=None, initial_s
     """Fused recurrent update (page "core.ssm.ops.gdp.fused_recurrent").
 
     Returns (o, final_state): final_state is `state` itself when a cache is
-    given, the dense final state when output_final_state, else None.  o and a
-    dense final state are allocated here with torch when not passed in."""
+    given, the dense final state when output_final_state, else None.  o (of
+    v's dtype) and a dense final state are allocated here with torch when not
+    passed in."""
     if o is None:
-        o = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     if state is None and output_final_state and final_state is None:
         N = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
         dt = initial_state.dtype if initial_state is not None else torch.float32

@@ -5,8 +5,8 @@
 Every source is compiled by hipcc for gfx950 only, with contraction off (the
 kernels spell out each fused multiply-add they want, which keeps the forward,
 verify and fold kernels bit-identical) and packed-fp32 VALU instructions
-disabled.  The recurrence tables (one per state type and kernel mode) are
-separate translation units, compiled in parallel, then linked.
+disabled.  The recurrence tables (one per work type, state type and kernel
+mode) are separate translation units, compiled in parallel, then linked.
 """
 from __future__ import annotations
 
@@ -22,9 +22,11 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdr.so")
 SOURCES = [os.path.join(CSRC, "gdr_api.cpp"), os.path.join(CSRC, "gdr_kernels.hip")]
 TABLE_SOURCE = os.path.join(CSRC, "gdr_rec_table.hip")
-# (state storage type, kernel mode) of each recurrence table: modes kPlain 0,
-# kVerify 1, kSnap 2, plus kBetaCols 4 (per-column beta).
-TABLES = [(st, mode) for st in ("uint16_t", "float") for mode in (0, 1, 2, 4, 6)]
+# (work type, state storage type, kernel mode) of each recurrence table:
+# types float or uint16_t (bf16 bits); modes kPlain 0, kVerify 1, kSnap 2,
+# plus kBetaCols 4 (per-column beta).
+TABLES = [(wt, st, mode) for wt in ("float", "uint16_t") for st in ("uint16_t", "float")
+          for mode in (0, 1, 2, 4, 6)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -49,10 +51,10 @@ def compile_commands(objdir, defines=()):
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         jobs.append((obj, [HIPCC, *FLAGS, *defines, "-x", "hip", "-c", src, "-o", obj]))
-    for st, mode in TABLES:
-        obj = os.path.join(objdir, f"table_{st}_{mode}.o")
-        jobs.append((obj, [HIPCC, *FLAGS, *defines, f"-DGDR_ST={st}", f"-DGDR_MODE={mode}",
-                           "-x", "hip", "-c", TABLE_SOURCE, "-o", obj]))
+    for wt, st, mode in TABLES:
+        obj = os.path.join(objdir, f"table_{wt}_{st}_{mode}.o")
+        jobs.append((obj, [HIPCC, *FLAGS, *defines, f"-DGDR_WT={wt}", f"-DGDR_ST={st}",
+                           f"-DGDR_MODE={mode}", "-x", "hip", "-c", TABLE_SOURCE, "-o", obj]))
     return jobs
 
 

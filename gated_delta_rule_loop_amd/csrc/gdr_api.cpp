@@ -83,6 +83,17 @@ int check_index_vec(const char* fn, const char* name, const gdr_tensor* t, int64
     return GDR_OK;
 }
 
+// Every per-token tensor of a call shares the work dtype (f32 or bf16).
+int check_work_dtype(const char* fn, const char* name, const gdr_tensor* t, int32_t work) {
+    if (present(t) && t->dtype != work)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s is %s but the work dtype is %s", fn, name,
+                    dtype_name(t->dtype), dtype_name(work));
+    return GDR_OK;
+}
+
+// Outer-stride multiple (in elements) that keeps 16-byte rows for a dtype.
+int64_t vec_mult(int32_t dtype) { return dtype == GDR_DTYPE_BF16 ? 8 : 4; }
+
 bool head_dim_built(int64_t K) { return K == 16 || K == 32 || K == 64 || K == 128; }
 
 // State-like tensor [slots, nv, K, V] with a dense K x V block per head.
@@ -185,19 +196,23 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     if ((rc = check_index_vec(fn, "input_row_offsets", offsets, B + 1))) return rc;
     const int64_t conv = 2 * nk * K + nv * V;
     const int64_t qkv_shape[2] = {-1, conv};
-    if ((rc = check_tensor(fn, "qkv_conv_output", qkv, 2, qkv_shape, true, false, false)))
+    if ((rc = check_tensor(fn, "qkv_conv_output", qkv, 2, qkv_shape, true, true, false)))
         return rc;
-    if ((rc = check_layout(fn, "qkv_conv_output", qkv, 4))) return rc;
+    const int32_t work = qkv->dtype;
+    if ((rc = check_layout(fn, "qkv_conv_output", qkv, vec_mult(work)))) return rc;
     const int64_t T = qkv->shape[0];
     const int64_t gate_shape[2] = {T, nv};
-    if ((rc = check_tensor(fn, "decay_per_token", decay, 2, gate_shape, true, false, false)))
+    if ((rc = check_tensor(fn, "decay_per_token", decay, 2, gate_shape, true, true, false)) ||
+        (rc = check_work_dtype(fn, "decay_per_token", decay, work)))
         return rc;
-    if ((rc = check_tensor(fn, "beta_per_token", beta, 2, gate_shape, true, false, false)))
+    if ((rc = check_tensor(fn, "beta_per_token", beta, 2, gate_shape, true, true, false)) ||
+        (rc = check_work_dtype(fn, "beta_per_token", beta, work)))
         return rc;
     const int64_t out_shape[2] = {T, nv * V};
-    if ((rc = check_tensor(fn, "recurrence_output", out, 2, out_shape, true, false, false)))
+    if ((rc = check_tensor(fn, "recurrence_output", out, 2, out_shape, true, true, false)) ||
+        (rc = check_work_dtype(fn, "recurrence_output", out, work)))
         return rc;
-    if ((rc = check_layout(fn, "recurrence_output", out, 4))) return rc;
+    if ((rc = check_layout(fn, "recurrence_output", out, vec_mult(work)))) return rc;
     const int64_t G = nv / nk;
 
     gdr::RecParams p{};
@@ -241,22 +256,23 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     p.G = static_cast<int32_t>(G);
     p.parts = static_cast<int32_t>(units / s.wpg);
     p.offsets = as_u32(offsets);
-    const float* x = static_cast<const float*>(qkv->data);
+    const char* x = static_cast<const char*>(qkv->data);
+    const int64_t es = work == GDR_DTYPE_BF16 ? 2 : 4;
     const int64_t ch = qkv->stride[1];
     p.q = x;
-    p.k = x + nk * K * ch;
-    p.v = x + 2 * nk * K * ch;
+    p.k = x + nk * K * ch * es;
+    p.v = x + 2 * nk * K * ch * es;
     p.q_tok = p.k_tok = p.v_tok = qkv->stride[0];
     p.q_head = p.k_head = K;
     p.v_head = V;
-    p.gate = static_cast<const float*>(decay->data);
+    p.gate = decay->data;
     p.g_tok = decay->stride[0];
     p.g_head = decay->stride[1];
     p.gate_is_log = 0;
-    p.beta = static_cast<const float*>(beta->data);
+    p.beta = beta->data;
     p.b_tok = beta->stride[0];
     p.b_head = beta->stride[1];
-    p.out = static_cast<float*>(out->data);
+    p.out = out->data;
     p.o_tok = out->stride[0];
     p.o_head = V;
     p.slot_idx = as_u32(slot_idx);
@@ -273,7 +289,8 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
     const gdr::StateType st =
         state->dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
-    return hip_status(fn, gdr::launch_recurrence(p, s, st, static_cast<hipStream_t>(stream)));
+    return hip_status(fn, gdr::launch_recurrence(p, s, st, work == GDR_DTYPE_BF16,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -376,10 +393,15 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     int rc;
     if (flags & ~GDR_FLAG_L2NORM_QK)
         return fail(GDR_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
-    if ((rc = check_tensor(fn, "q", q, 4, nullptr, true, false, false))) return rc;
+    if ((rc = check_tensor(fn, "q", q, 4, nullptr, true, true, false))) return rc;
+    const int32_t work = q->dtype;
     const int64_t B = q->shape[0], T = q->shape[1], H = q->shape[2], K = q->shape[3];
-    if ((rc = check_tensor(fn, "k", k, 4, q->shape, true, false, false))) return rc;
-    if ((rc = check_tensor(fn, "v", v, 4, nullptr, true, false, false))) return rc;
+    if ((rc = check_tensor(fn, "k", k, 4, q->shape, true, true, false)) ||
+        (rc = check_work_dtype(fn, "k", k, work)))
+        return rc;
+    if ((rc = check_tensor(fn, "v", v, 4, nullptr, true, true, false)) ||
+        (rc = check_work_dtype(fn, "v", v, work)))
+        return rc;
     const int64_t HV = v->shape[2], V = v->shape[3];
     if (v->shape[0] != B || v->shape[1] != T)
         return fail(GDR_ERR_INVALID_ARG, "%s: v must be [B, T, HV, V] like q", fn);
@@ -390,20 +412,28 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
         return fail(GDR_ERR_UNSUPPORTED, "%s: head dim %lld not built (16, 32, 64, 128)", fn,
                     static_cast<long long>(K));
     if ((rc = check_layout(fn, "q", q, 1)) || (rc = check_layout(fn, "k", k, 1)) ||
-        (rc = check_layout(fn, "v", v, 4)))
+        (rc = check_layout(fn, "v", v, vec_mult(work))))
         return rc;
     const int64_t gshape[3] = {B, T, HV};
-    if (present(g) && (rc = check_tensor(fn, "g", g, 3, gshape, true, false, false))) return rc;
+    if (present(g) && ((rc = check_tensor(fn, "g", g, 3, gshape, true, true, false)) ||
+                       (rc = check_work_dtype(fn, "g", g, work))))
+        return rc;
     const bool beta_cols = present(beta) && beta->ndim == 4;
     if (beta_cols) {  // one beta per value column: [B, T, HV, V]
-        if ((rc = check_tensor(fn, "beta", beta, 4, v->shape, true, false, false))) return rc;
-        if ((rc = check_layout(fn, "beta", beta, 4))) return rc;
+        if ((rc = check_tensor(fn, "beta", beta, 4, v->shape, true, true, false)) ||
+            (rc = check_work_dtype(fn, "beta", beta, work)))
+            return rc;
+        if ((rc = check_layout(fn, "beta", beta, vec_mult(work)))) return rc;
     } else if (present(beta)) {
-        if ((rc = check_tensor(fn, "beta", beta, 3, gshape, true, false, false))) return rc;
+        if ((rc = check_tensor(fn, "beta", beta, 3, gshape, true, true, false)) ||
+            (rc = check_work_dtype(fn, "beta", beta, work)))
+            return rc;
     }
     const int64_t oshape[4] = {B, T, HV, V};
-    if ((rc = check_tensor(fn, "o", o, 4, oshape, true, false, false))) return rc;
-    if ((rc = check_layout(fn, "o", o, 4))) return rc;
+    if ((rc = check_tensor(fn, "o", o, 4, oshape, true, true, false)) ||
+        (rc = check_work_dtype(fn, "o", o, work)))
+        return rc;
+    if ((rc = check_layout(fn, "o", o, vec_mult(work)))) return rc;
 
     int64_t N = B;
     if (present(cu_seqlens)) {
@@ -481,30 +511,31 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     p.parts = static_cast<int32_t>(units / s.wpg);
     p.dense_len = static_cast<int32_t>(T);
     p.offsets = as_u32(cu_seqlens);
-    p.q = static_cast<const float*>(q->data);
+    p.q = q->data;
     p.q_seq = q->stride[0]; p.q_tok = q->stride[1]; p.q_head = q->stride[2];
-    p.k = static_cast<const float*>(k->data);
+    p.k = k->data;
     p.k_seq = k->stride[0]; p.k_tok = k->stride[1]; p.k_head = k->stride[2];
-    p.v = static_cast<const float*>(v->data);
+    p.v = v->data;
     p.v_seq = v->stride[0]; p.v_tok = v->stride[1]; p.v_head = v->stride[2];
     if (present(g)) {
-        p.gate = static_cast<const float*>(g->data);
+        p.gate = g->data;
         p.g_seq = g->stride[0]; p.g_tok = g->stride[1]; p.g_head = g->stride[2];
         p.gate_is_log = 1;
     }
     if (present(beta)) {
-        p.beta = static_cast<const float*>(beta->data);
+        p.beta = beta->data;
         p.b_seq = beta->stride[0]; p.b_tok = beta->stride[1]; p.b_head = beta->stride[2];
         p.beta_cols = beta_cols ? 1 : 0;
     }
-    p.out = static_cast<float*>(o->data);
+    p.out = o->data;
     p.o_seq = o->stride[0]; p.o_tok = o->stride[1]; p.o_head = o->stride[2];
     p.spt = steps_per_token;
     p.scale = resolve_scale(scale, K);
     p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
     const gdr::StateType st =
         st_dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
-    return hip_status(fn, gdr::launch_recurrence(p, s, st, static_cast<hipStream_t>(stream)));
+    return hip_status(fn, gdr::launch_recurrence(p, s, st, work == GDR_DTYPE_BF16,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indices,

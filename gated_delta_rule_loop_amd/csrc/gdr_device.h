@@ -235,7 +235,28 @@ struct Item {
     bool pad, record;
 };
 
-template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW>
+// One element of a per-token tensor (float32, or bf16 bits widened exactly).
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+
+// The same in two steps: the raw element (bf16 bits zero-extended, held in a
+// float register), then its value.  Staged loads keep the raw form until
+// their first arithmetic use, so no conversion forces an early wait.
+__device__ __forceinline__ float load_raw(const float* p) { return *p; }
+__device__ __forceinline__ float load_raw(const uint16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p));
+}
+template <typename WT>
+__device__ __forceinline__ float widen_raw(float raw) {
+    if constexpr (sizeof(WT) == 2) return __uint_as_float(__float_as_uint(raw) << 16);
+    return raw;
+}
+
+// ST: state storage type; WT: per-token input/output type (float, or
+// uint16_t holding bf16 bits).  Arithmetic is float32 either way.
+template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT>
 struct Rec {
     static constexpr int V = K;
     static constexpr int R = K / kRowGroups;
@@ -300,8 +321,8 @@ struct Rec {
         return it;
     }
 
-    __device__ static float* out_ptr(const RecParams& p, const Item& it) {
-        return p.out + it.ro + static_cast<int64_t>(it.hv) * p.o_head + it.j0;
+    __device__ static WT* out_ptr(const RecParams& p, const Item& it) {
+        return static_cast<WT*>(p.out) + it.ro + static_cast<int64_t>(it.hv) * p.o_head + it.j0;
     }
 
     __device__ static const ST* src_ptr(const RecParams& p, const Item& it) {
@@ -316,7 +337,7 @@ struct Rec {
         float z[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) z[c] = 0.0f;
-        float* outp = out_ptr(p, it);
+        WT* outp = out_ptr(p, it);
         for (int t = 0; t < it.L; ++t) store_cols<CPL>(outp + t * p.o_tok, z);
     }
 
@@ -354,61 +375,74 @@ struct Rec {
                    kg, scale, S);
     }
 
-    // v, or the per-column beta, of a chunk: VPL consecutive floats per lane
-    // of the wave's C x BV block.
-    __device__ static void load_block(const float* base, int64_t tok, int L, int tc, int lane,
+    // The raw form (see load_raw) of 1.0.
+    __device__ static float raw_one() {
+        if constexpr (sizeof(WT) == 2) return __uint_as_float(0x3F80u);
+        return 1.0f;
+    }
+
+    // v, or the per-column beta, of a chunk: VPL consecutive elements per
+    // lane of the wave's C x BV block (one vector load).  Lanes past the block
+    // or the row re-read a valid vector and keep zeros.
+    __device__ static void load_block(const WT* base, int64_t tok, int L, int tc, int lane,
                                       float (&dst)[VPL]) {
-        const int flat = lane * VPL;
+        const int flat = min(lane * VPL, VTOT - VPL);
         const int tau = flat / BV;
         const int col = flat - tau * BV;
         const int t = tc + tau;
-        const bool ok = flat < VTOT && t < L;
-        const float* vp = base + t * tok + col;
-        if constexpr (VPL == 4) {
-            float4 x = ok ? *reinterpret_cast<const float4*>(vp) : make_float4(0, 0, 0, 0);
-            dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
-        } else if constexpr (VPL == 2) {
-            float2 x = ok ? *reinterpret_cast<const float2*>(vp) : make_float2(0, 0);
-            dst[0] = x.x; dst[1] = x.y;
-        } else {
+        const bool ok = lane * VPL < VTOT && t < L;
+        float x[VPL];
+        load_cols<VPL>(base + min(t, L - 1) * tok + col, x);
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) dst[i] = ok ? vp[i] : 0.0f;
-        }
+        for (int i = 0; i < VPL; ++i) dst[i] = ok ? x[i] : 0.0f;
     }
 
-    // Global loads of chunk c of an item into registers.
+    // Global loads of chunk c of an item into registers.  Each load is
+    // unconditional - an index past the row's end or the head dim is clamped
+    // to a valid element whose value is then replaced - so that a stage's
+    // loads issue back to back and retire under a single wait.  The decay is
+    // kept raw (exp is applied in commit_stage, after that wait).
     template <bool BC>
     __device__ static void load_stage(const RecParams& p, const Item& it, int c, Stage& s,
                                       int w, int lane) {
         const int tc = c * C;
+        const int last = it.L - 1;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int tau = w + i * WPG;
             const int t = tc + tau;
-            const bool ok = tau < C && t < it.L;
+            const int64_t tl = min(t, last);
+            const WT* qp = static_cast<const WT*>(p.q) + it.rq + tl * p.q_tok + it.h * p.q_head;
+            const WT* kp = static_cast<const WT*>(p.k) + it.rk + tl * p.k_tok + it.h * p.k_head;
 #pragma unroll
             for (int e = 0; e < QK; ++e) {
                 const int idx = lane + 64 * e;
-                const bool in = ok && idx < K;
-                s.q[i][e] = in ? p.q[it.rq + t * p.q_tok + it.h * p.q_head + idx] : 0.0f;
-                s.k[i][e] = in ? p.k[it.rk + t * p.k_tok + it.h * p.k_head + idx] : 0.0f;
+                const bool in = tau < C && t < it.L && idx < K;
+                float q = 0.0f, k = 0.0f;  // raw (see load_raw); 0 is 0 either way
+                if (tau < C) {  // wave-uniform: waves past the chunk load nothing
+                    q = load_raw(qp + min(idx, K - 1));
+                    k = load_raw(kp + min(idx, K - 1));
+                }
+                s.q[i][e] = in ? q : 0.0f;
+                s.k[i][e] = in ? k : 0.0f;
             }
         }
-        load_block(p.v + it.rv + it.hv * p.v_head + it.vt * BV, p.v_tok, it.L, tc, lane, s.v);
+        load_block(static_cast<const WT*>(p.v) + it.rv + it.hv * p.v_head + it.vt * BV, p.v_tok,
+                   it.L, tc, lane, s.v);
         if constexpr (BC)
-            load_block(p.beta + it.rb + it.hv * p.b_head + it.vt * BV, p.b_tok, it.L, tc, lane,
-                       s.bv);
-        {
-            const int t = tc + lane;
-            const bool ok = lane < C && t < it.L;
-            s.a = 1.0f;
-            s.b = 1.0f;
-            if (ok && p.gate) {
-                const float g = p.gate[it.rg + t * p.g_tok + it.hv * p.g_head];
-                s.a = p.gate_is_log ? expf(g) : g;
-            }
-            if (!BC && ok && p.beta) s.b = p.beta[it.rb + t * p.b_tok + it.hv * p.b_head];
-        }
+            load_block(static_cast<const WT*>(p.beta) + it.rb + it.hv * p.b_head + it.vt * BV,
+                       p.b_tok, it.L, tc, lane, s.bv);
+        const bool ok = lane < C && tc + lane < it.L;
+        const int64_t tl = min(tc + min(lane, C - 1), last);
+        // raw gates; an absent or out-of-range gate stages the raw form of 1
+        // (of 0 for a log decay, exp(0) = 1)
+        float g = 0.0f, b = 0.0f;
+        if (p.gate)
+            g = load_raw(static_cast<const WT*>(p.gate) + it.rg + tl * p.g_tok + it.hv * p.g_head);
+        if (!BC && p.beta)
+            b = load_raw(static_cast<const WT*>(p.beta) + it.rb + tl * p.b_tok + it.hv * p.b_head);
+        s.a = ok && p.gate ? g : (p.gate_is_log ? 0.0f : raw_one());
+        s.b = ok && !BC && p.beta ? b : raw_one();
     }
 
     // Norms of the staged tokens, then k_hat, q_hat*scale, v and gates to LDS.
@@ -424,14 +458,20 @@ struct Rec {
         for (int i = 0; i < SPW; ++i) {
             const int tau = w + i * WPG;
             if (tau >= C) break;
+            float qv[QK], kv[QK];
+#pragma unroll
+            for (int e = 0; e < QK; ++e) {
+                qv[e] = widen_raw<WT>(s.q[i][e]);
+                kv[e] = widen_raw<WT>(s.k[i][e]);
+            }
             float rk = 1.0f, rqs = p.scale;
             if (p.l2norm) {
-                float kk = s.k[i][0] * s.k[i][0];
-                float qq = s.q[i][0] * s.q[i][0];
+                float kk = kv[0] * kv[0];
+                float qq = qv[0] * qv[0];
 #pragma unroll
                 for (int e = 1; e < QK; ++e) {
-                    kk = __builtin_fmaf(s.k[i][e], s.k[i][e], kk);
-                    qq = __builtin_fmaf(s.q[i][e], s.q[i][e], qq);
+                    kk = __builtin_fmaf(kv[e], kv[e], kk);
+                    qq = __builtin_fmaf(qv[e], qv[e], qq);
                 }
                 kk = sum_wave(kk);
                 qq = sum_wave(qq);
@@ -443,9 +483,9 @@ struct Rec {
             for (int e = 0; e < QK; ++e) {
                 const int idx = lane + 64 * e;
                 if (idx < K) {
-                    const float kh = s.k[i][e] * rk;
+                    const float kh = kv[e] * rk;
                     B[OFF_K + tau * KP + pad_index<R>(idx)] = kh;
-                    B[OFF_Q + tau * KP + pad_index<R>(idx)] = s.q[i][e] * rqs;
+                    B[OFF_Q + tau * KP + pad_index<R>(idx)] = qv[e] * rqs;
                     if (rec_k) ring_put(p, rec + (tc + tau) * p.ring_tok + idx, kh);
                 }
             }
@@ -457,8 +497,9 @@ struct Rec {
             if (BC && flat < VTOT) B[OFF_BV + w * VTOT + flat] = s.bv[i];
         }
         if (lane < C) {
-            B[OFF_A + w * C + lane] = s.a;
-            B[OFF_B + w * C + lane] = s.b;
+            const float a = widen_raw<WT>(s.a);
+            B[OFF_A + w * C + lane] = p.gate && p.gate_is_log ? expf(a) : a;
+            B[OFF_B + w * C + lane] = widen_raw<WT>(s.b);
         }
     }
 
@@ -472,7 +513,7 @@ struct Rec {
         const int vc = col_chunk(lane) * CPL;
         const int tc = c * C;
         const int Lc = min(C, it.L - tc);
-        float* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
+        WT* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
         int64_t rec = 0;  // ring element offset of this token's record
         if (REC && it.record)
             rec = static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
@@ -597,9 +638,9 @@ struct Rec {
 template <int C>
 constexpr int kMinWaves = C == 1 ? 4 : 1;
 
-template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, int MODE>
+template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
 __global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecParams p) {
-    using Q = Rec<K, CPL, C, WPG, ST, KG_LOW>;
+    using Q = Rec<K, CPL, C, WPG, ST, KG_LOW, WT>;
     __shared__ __attribute__((aligned(16))) float lds[2 * Q::template buf<(MODE & kBetaCols) != 0>()];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -610,43 +651,45 @@ __global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecPa
         return;
     }
     if (it.L <= 0) return;
+    // The first stage's loads are issued before the state's, so that both
+    // are in flight together.
+    typename Q::Stage st;
+    Q::template load_stage<(MODE & kBetaCols) != 0>(p, it, 0, st, w, lane);
     float S[Q::R][CPL];
     Q::load_state(p, it, kg, S);
     float scale = 1.0f;
-    typename Q::Stage st;
-    Q::template load_stage<(MODE & kBetaCols) != 0>(p, it, 0, st, w, lane);
     Q::template run_item<MODE>(p, it, S, scale, st, lds, w, lane);
     Q::store_state(p, it, kg, scale, S);
 }
 
 }  // namespace
 
-template <int K, int CPL, int C, typename ST, bool KG_LOW, int MODE>
+template <int K, int CPL, int C, typename ST, bool KG_LOW, typename WT, int MODE>
 static hipError_t launch_rec_mode(const RecParams& p, int wpg, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.rows) * p.nk * p.parts);
     constexpr int TILES = K / (kLanesPerRow * CPL);
     if constexpr (TILES % 4 == 0) {  // every head splits into a multiple of 4 waves
         if (wpg != 4) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, MODE>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, WT, MODE>), grid, dim3(256), 0, stream, p);
     } else {
         switch (wpg) {
-            case 1: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 1, ST, KG_LOW, MODE>), grid, dim3(64), 0, stream, p); break;
-            case 2: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 2, ST, KG_LOW, MODE>), grid, dim3(128), 0, stream, p); break;
-            case 4: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, MODE>), grid, dim3(256), 0, stream, p); break;
+            case 1: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 1, ST, KG_LOW, WT, MODE>), grid, dim3(64), 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 2, ST, KG_LOW, WT, MODE>), grid, dim3(128), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, WT, MODE>), grid, dim3(256), 0, stream, p); break;
             default: return hipErrorInvalidValue;
         }
     }
     return hipGetLastError();
 }
 
-// One (state type, mode) table of recurrence launch shapes.  Each table is
-// instantiated in a translation unit of its own (gdr_rec_table.hip), so the
-// library compiles in parallel.
-template <typename ST, int MODE>
+// One (work type, state type, mode) table of recurrence launch shapes.  Each
+// table is instantiated in a translation unit of its own (gdr_rec_table.hip),
+// so the library compiles in parallel.
+template <typename WT, typename ST, int MODE>
 hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_t stream) {
 #define GDR_REC_CASE(KK, CC, CH, KL)                                              \
     if (s.K == KK && s.cpl == CC && s.chunk == CH && s.kg_low == KL)             \
-        return launch_rec_mode<KK, CC, CH, ST, KL, MODE>(p, s.wpg, stream);
+        return launch_rec_mode<KK, CC, CH, ST, KL, WT, MODE>(p, s.wpg, stream);
     GDR_REC_CASE(128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
     GDR_REC_CASE(128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
     GDR_REC_CASE(128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)

@@ -19,14 +19,15 @@ struct RecParams {
     int32_t dense_len;   // tokens per row when offsets == nullptr
     const uint32_t* offsets;
 
-    const float* q; int64_t q_seq, q_tok, q_head;
-    const float* k; int64_t k_seq, k_tok, k_head;
-    const float* v; int64_t v_seq, v_tok, v_head;
-    const float* gate; int64_t g_seq, g_tok, g_head;   // nullptr: a = 1
+    // Per-token tensors, all of the work type (float32 or bf16).
+    const void* q; int64_t q_seq, q_tok, q_head;
+    const void* k; int64_t k_seq, k_tok, k_head;
+    const void* v; int64_t v_seq, v_tok, v_head;
+    const void* gate; int64_t g_seq, g_tok, g_head;    // nullptr: a = 1
     int32_t gate_is_log;                               // a = exp(gate)
-    const float* beta; int64_t b_seq, b_tok, b_head;   // nullptr: beta = 1
+    const void* beta; int64_t b_seq, b_tok, b_head;    // nullptr: beta = 1
     int32_t beta_cols;                                 // beta has a unit-stride V axis
-    float* out; int64_t o_seq, o_tok, o_head;
+    void* out; int64_t o_seq, o_tok, o_head;
 
     // State: slot = slot_idx[row] (nullptr: slot = row).  kPadSlot pads.
     const uint32_t* slot_idx;
@@ -77,7 +78,7 @@ struct LaunchShape {
 
 // Host-side launchers (defined next to the kernels).  Return hipError_t.
 hipError_t launch_recurrence(const RecParams& p, const LaunchShape& s, StateType st,
-                             hipStream_t stream);
+                             bool work_bf16, hipStream_t stream);
 hipError_t launch_fold(const FoldParams& p, const LaunchShape& s, StateType st,
                        hipStream_t stream);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t stream);

@@ -7,26 +7,46 @@
 namespace gdr {
 
 // Recurrence tables, one translation unit each (gdr_rec_table.hip).
-extern template hipError_t launch_rec_table<uint16_t, kPlain>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<uint16_t, kVerify>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<uint16_t, kSnap>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<uint16_t, kPlain | kBetaCols>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<uint16_t, kSnap | kBetaCols>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<float, kPlain>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<float, kVerify>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<float, kSnap>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<float, kPlain | kBetaCols>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
-extern template hipError_t launch_rec_table<float, kSnap | kBetaCols>(const RecParams&, const LaunchShape&,
-                                                                hipStream_t);
+extern template hipError_t launch_rec_table<float, uint16_t, kPlain>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, uint16_t, kVerify>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, uint16_t, kSnap>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, uint16_t, kPlain | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, uint16_t, kSnap | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, float, kPlain>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, float, kVerify>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, float, kSnap>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, float, kPlain | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<float, float, kSnap | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, uint16_t, kPlain>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, uint16_t, kVerify>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, uint16_t, kSnap>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, uint16_t, kPlain | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, uint16_t, kSnap | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, float, kPlain>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, float, kVerify>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, float, kSnap>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, float, kPlain | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
+extern template hipError_t launch_rec_table<uint16_t, float, kSnap | kBetaCols>(const RecParams&,
+                                                                  const LaunchShape&, hipStream_t);
 
 namespace {
 
@@ -158,24 +178,31 @@ hipError_t launch_rollback(const RollbackParams& p, hipStream_t stream) {
 
 // ------------------------------------------------------------- dispatch ---
 
-template <typename ST>
+template <typename WT, typename ST>
 static hipError_t launch_rec_st(const RecParams& p, const LaunchShape& s, hipStream_t stream) {
     if (p.ring) {  // the packed verify has head-wise beta only
         if (p.beta_cols) return hipErrorInvalidValue;
-        return launch_rec_table<ST, kVerify>(p, s, stream);
+        return launch_rec_table<WT, ST, kVerify>(p, s, stream);
     }
     if (p.beta_cols) {
-        if (p.snap) return launch_rec_table<ST, kSnap | kBetaCols>(p, s, stream);
-        return launch_rec_table<ST, kPlain | kBetaCols>(p, s, stream);
+        if (p.snap) return launch_rec_table<WT, ST, kSnap | kBetaCols>(p, s, stream);
+        return launch_rec_table<WT, ST, kPlain | kBetaCols>(p, s, stream);
     }
-    if (p.snap) return launch_rec_table<ST, kSnap>(p, s, stream);
-    return launch_rec_table<ST, kPlain>(p, s, stream);
+    if (p.snap) return launch_rec_table<WT, ST, kSnap>(p, s, stream);
+    return launch_rec_table<WT, ST, kPlain>(p, s, stream);
+}
+
+template <typename WT>
+static hipError_t launch_rec_wt(const RecParams& p, const LaunchShape& s, StateType st,
+                                hipStream_t stream) {
+    return st == StateType::BF16 ? launch_rec_st<WT, uint16_t>(p, s, stream)
+                                 : launch_rec_st<WT, float>(p, s, stream);
 }
 
 hipError_t launch_recurrence(const RecParams& p, const LaunchShape& s, StateType st,
-                             hipStream_t stream) {
-    return st == StateType::BF16 ? launch_rec_st<uint16_t>(p, s, stream)
-                                 : launch_rec_st<float>(p, s, stream);
+                             bool work_bf16, hipStream_t stream) {
+    return work_bf16 ? launch_rec_wt<uint16_t>(p, s, st, stream)
+                     : launch_rec_wt<float>(p, s, st, stream);
 }
 
 template <int K, int CPL, typename ST, typename RT>

@@ -48,6 +48,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+WORK_KEYS = ("qkv", "decay", "beta", "q", "k", "v", "g")
+
+
+def bf16_work(w: dict) -> dict:
+    """The same workload with its per-token inputs (qkv, decay, beta, or q, k,
+    v, g, beta) rounded to bfloat16, as uint16 bits."""
+    out = dict(w)
+    for key in WORK_KEYS:
+        a = out.get(key)
+        if a is not None and a.dtype == np.float32:
+            out[key] = to_bf16_bits(a)
+    return out
+
+
 def ring_record_stride(group: int, K: int, V: int, align: int = 32) -> int:
     """A record stride of at least K + group*(V+1) elements, rounded up."""
     need = K + group * (V + 1)

@@ -72,19 +72,27 @@ typedef struct gdr_tensor {
 
 /*
  * gdr_recurrence_fwd - slot-indexed ragged forward.
- * Source: page "gated_delta_recurrence_fwd_gpu" (summary and Args).
+ * Source: page "gated_delta_recurrence_fwd_gpu" (summary and Args); the
+ * work dtype of the per-token tensors as on page
+ * "gated_delta_recurrence_verify_ring_gpu" (Parameters, work_dtype).
  *
- *   recurrence_output [T, nv*V] f32   written for every token (out)
+ * The per-token tensors (qkv_conv_output, decay_per_token, beta_per_token,
+ * recurrence_output) share one work dtype, f32 or bf16; the arithmetic is
+ * float32 either way (bf16 inputs widen exactly, bf16 outputs are rounded to
+ * nearest even once).  2-D per-token tensors with vector accesses
+ * (qkv_conv_output, recurrence_output) need 16-byte rows.
+ *
+ *   recurrence_output [T, nv*V] work  written for every token (out)
  *   recurrent_state   [slots, nv, K, V] bf16|f32, V contiguous, each head's
  *                     K x V block dense (in/out: the slot of each row is read
  *                     and written back in place; rows of length 0 are not
  *                     touched)
  *   slot_idx          [B] u32|i32     pool slot per row
- *   qkv_conv_output   [T, 2*nk*K + nv*V] f32: q of key head h at channels
+ *   qkv_conv_output   [T, 2*nk*K + nv*V] work: q of key head h at channels
  *                     [h*K, (h+1)*K), k at nk*K + ..., v of value head hv at
  *                     2*nk*K + hv*V + ...
- *   decay_per_token   [T, nv] f32     multiplicative decay a_t
- *   beta_per_token    [T, nv] f32     beta gate
+ *   decay_per_token   [T, nv] work    multiplicative decay a_t
+ *   beta_per_token    [T, nv] work    beta gate
  *   input_row_offsets [B+1] u32|i32   row b spans [off[b], off[b+1])
  *   scale             <= 0 or NaN selects 1/sqrt(K)
  *   flags             GDR_FLAG_L2NORM_QK (the page always normalises; pass it)
@@ -157,10 +165,11 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
  * (fused_recurrent_gated_delta_rule_update parameters; module summary on
  * Householder folding and intermediate states).
  *
- *   q, k              [B, T, H, K] f32
- *   v                 [B, T, HV, V] f32
- *   g                 [B, T, HV] f32 log decay (a = exp(g)), or absent (a = 1)
- *   beta              [B, T, HV] f32, or [B, T, HV, V] f32 with unit stride
+ *   q, k              [B, T, H, K] work dtype: f32 or bf16, shared by q, k,
+ *                     v, g, beta and o (float32 arithmetic either way)
+ *   v                 [B, T, HV, V] work
+ *   g                 [B, T, HV] work log decay (a = exp(g)), or absent (a = 1)
+ *   beta              [B, T, HV] work, or [B, T, HV, V] work with unit stride
  *                     over V (one beta per value column), or absent (beta = 1)
  *   scale             <= 0 or NaN selects K^-0.5
  *   initial_state     [N, HV, K, V] bf16|f32 or absent (zeros); ignored when
@@ -181,7 +190,7 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
  *                     (i+1)*steps_per_token steps; steps past shape[1] are not
  *                     snapshotted.
  *   steps_per_token   >= 1
- *   o                 [B, T, HV, V] f32 (out)
+ *   o                 [B, T, HV, V] work (out)
  */
 int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const gdr_tensor* v,
                                const gdr_tensor* g, const gdr_tensor* beta, float scale,

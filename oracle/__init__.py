@@ -86,6 +86,25 @@ def _state_copy(a):
     raise TypeError(f"state arrays must be float32 or uint16 (bf16 bits), got {a.dtype}")
 
 
+def _work(arrays):
+    """Per-token inputs of one call: all float32, or all uint16 (bf16 bits),
+    the work dtype.  Returns (float32 arrays, is_bf16); bf16 widens exactly."""
+    kinds = {a.dtype for a in arrays if a is not None}
+    if len(kinds) > 1:
+        raise TypeError("per-token inputs must share one work dtype")
+    bf = kinds == {np.dtype(np.uint16)}
+    conv = []
+    for a in arrays:
+        if a is None:
+            conv.append(None)
+        elif bf:
+            b = np.ascontiguousarray(a, dtype=np.uint16).astype(np.uint32) << 16
+            conv.append(b.view(np.float32))
+        else:
+            conv.append(np.ascontiguousarray(a, dtype=np.float32))
+    return conv, bf
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bits, nearest even (the oracle's own rounding)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -102,11 +121,13 @@ def recurrence_fwd(*, qkv, decay, beta, state, slot_idx, row_offsets, num_value_
                    num_key_heads, scale=None, l2norm=True):
     """Ragged slot-indexed forward ("gated_delta_recurrence_fwd_gpu").
 
-    Returns (out [T, nv*V] float32, state_after)."""
+    qkv, decay and beta share the work dtype: float32, or uint16 bf16 bits
+    (verify page, work_dtype), which widen exactly; the output is then rounded
+    to bf16 once.  Returns (out [T, nv*V] of the work dtype, state_after)."""
     lib = _load()
     st, bf = _state_copy(state)
     K, V = st.shape[2], st.shape[3]
-    qkv, decay, beta = _f32(qkv), _f32(decay), _f32(beta)
+    (qkv, decay, beta), work_bf16 = _work((qkv, decay, beta))
     off = np.ascontiguousarray(row_offsets, dtype=np.uint32)
     sl = np.ascontiguousarray(slot_idx, dtype=np.uint32)
     B = sl.shape[0]
@@ -118,7 +139,7 @@ def recurrence_fwd(*, qkv, decay, beta, state, slot_idx, row_offsets, num_value_
         bf, _p(st), ctypes.c_int64(st.shape[0]), _p(out), ctypes.c_float(sc), int(l2norm))
     if rc != 0:
         raise ValueError(f"oracle_recurrence_fwd failed: {rc}")
-    return out, st
+    return (bf16_round(out) if work_bf16 else out), st
 
 
 def ring_record_elements(group: int, K: int, V: int) -> int:
@@ -132,12 +153,12 @@ def recurrence_verify_ring(*, qkv, decay, beta, state, slot_idx, row_offsets, nu
     """Verify window with ring ("gated_delta_recurrence_verify_ring_gpu").
 
     ring: [ring_rows, nk, ring_len, rec_stride], float32 or uint16 (bf16 bits),
-    copied.
+    copied.  Work dtype as recurrence_fwd.
     Returns (out, state_after, ring_after)."""
     lib = _load()
     st, bf = _state_copy(state)
     K, V = st.shape[2], st.shape[3]
-    qkv, decay, beta = _f32(qkv), _f32(decay), _f32(beta)
+    (qkv, decay, beta), work_bf16 = _work((qkv, decay, beta))
     off = np.ascontiguousarray(row_offsets, dtype=np.uint32)
     sl = np.ascontiguousarray(slot_idx, dtype=np.uint32)
     rsl = np.ascontiguousarray(ring_slot_idx, dtype=np.uint32)
@@ -152,7 +173,7 @@ def recurrence_verify_ring(*, qkv, decay, beta, state, slot_idx, row_offsets, nu
         ctypes.c_int64(rg.shape[3]))
     if rc != 0:
         raise ValueError(f"oracle_recurrence_verify_ring failed: {rc}")
-    return out, st, rg
+    return (bf16_round(out) if work_bf16 else out), st, rg
 
 
 def state_fold(*, state, slot_idx, ring, ring_slot_idx, accepted, num_value_heads,
@@ -187,16 +208,15 @@ def fused_recurrent_update(*, q, k, v, g=None, beta=None, scale=None, initial_st
 
     q, k [B, T, H, K]; v [B, T, HV, V]; g, beta [B, T, HV] (beta may be
     [B, T, HV, V]); state [S, HV, K, V]; intermediate_states [S, T//spt, HV, K, V].
-    State-like arrays are float32 or uint16 (bf16 bits) and must share a dtype.
+    State-like arrays are float32 or uint16 (bf16 bits) and must share a dtype;
+    q, k, v, g, beta share the work dtype likewise, and o is of that dtype.
     Returns (o, final_state, intermediate_after): final_state is the updated
     pool copy when a pool is given, the dense final state when requested, else
     None; intermediate_after is the updated snapshot copy or None."""
     lib = _load()
-    q, k, v = _f32(q), _f32(k), _f32(v)
+    (q, k, v, g, beta), work_bf16 = _work((q, k, v, g, beta))
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
-    g = _f32(g)
-    beta = _f32(beta)
     beta_per_v = int(beta is not None and beta.ndim == 4)
     cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     N = B if cu is None else cu.shape[0] - 1
@@ -221,7 +241,7 @@ def fused_recurrent_update(*, q, k, v, g=None, beta=None, scale=None, initial_st
         _p(o))
     if rc != 0:
         raise ValueError(f"oracle_fused_recurrent_update failed: {rc}")
-    return o, (st if st is not None else final), inter
+    return (bf16_round(o) if work_bf16 else o), (st if st is not None else final), inter
 
 
 def snapshot_rollback(*, state, state_indices, intermediate_states, accepted):

@@ -35,12 +35,17 @@ def host(t):
     return t.numpy().copy()
 
 
+def _work_dtype(a):
+    return torch.bfloat16 if np.asarray(a).dtype == np.uint16 else torch.float32
+
+
 def gpu_fwd(w, *, scale=None, l2norm=True, out=None):
     d = {k: dev(w[k]) for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets")}
     T = w["qkv"].shape[0]
     V = w["state"].shape[3]
     if out is None:
-        out = torch.full((T, w["num_value_heads"] * V), float("nan"), device="cuda")
+        out = torch.full((T, w["num_value_heads"] * V), float("nan"), device="cuda",
+                         dtype=_work_dtype(w["qkv"]))
     sc = w.get("scale") if scale is None else scale
     gdr.gdr_recurrence_fwd(out, d["state"], d["slot_idx"], d["qkv"], d["decay"], d["beta"],
                            d["row_offsets"], num_value_heads=w["num_value_heads"],
@@ -55,7 +60,8 @@ def gpu_verify(w, *, ring=None, scale=None):
     rg = dev(w["ring"] if ring is None else ring)
     T = w["qkv"].shape[0]
     V = w["state"].shape[3]
-    out = torch.full((T, w["num_value_heads"] * V), float("nan"), device="cuda")
+    out = torch.full((T, w["num_value_heads"] * V), float("nan"), device="cuda",
+                     dtype=_work_dtype(w["qkv"]))
     gdr.gdr_recurrence_verify_ring(out, d["state"], d["slot_idx"], d["qkv"], d["decay"],
                                    d["beta"], d["row_offsets"], rg, d["ring_slot_idx"],
                                    num_value_heads=w["num_value_heads"],

@@ -462,6 +462,32 @@ def pin_bf16_ring():
     assert np.array_equal(s_b[w["slot_idx"][3]], st_f[w["slot_idx"][3]])
 
 
+def pin_bf16_work():
+    """Verify page, work_dtype bfloat16: bf16 per-token inputs widen exactly
+    and the output is rounded once, so the result is torch's bf16 cast of the
+    float32 run on the widened inputs, and the state is that run's, bit for
+    bit (forward, verify and fused entries)."""
+    w = small_packed(29, [3, 0, 6, 2], K=8, V=8, state_dtype="bf16")
+    wb = wl.bf16_work(w)
+    ww = dict(wb, **{k: wl.bf16_bits_to_f32(wb[k]) for k in ("qkv", "decay", "beta")})
+    out_b, st_b = run_fwd(wb)
+    out_w, st_w = run_fwd(ww)
+    assert out_b.dtype == np.uint16
+    assert np.array_equal(out_b, wl.to_bf16_bits(out_w))
+    assert np.array_equal(st_b, st_w)
+    rng = _rng(30)
+    g = wl.gdp_inputs(rng, B=3, S_draft=2, M=2, H=2, HV=4, K=8, V=8, slots=4, pad_frac=0.3,
+                      state_sigma=0.2)
+    gb = wl.bf16_work(g)
+    gw = dict(gb, **{k: wl.bf16_bits_to_f32(gb[k]) for k in ("q", "k", "v", "g", "beta")})
+    keys = ("q", "k", "v", "g", "beta", "state", "state_indices", "intermediate_states",
+            "steps_per_token", "use_qk_l2norm_in_kernel", "scale")
+    o_b, s_b, i_b = oracle.fused_recurrent_update(**{k: gb[k] for k in keys})
+    o_w, s_w, i_w = oracle.fused_recurrent_update(**{k: gw[k] for k in keys})
+    assert np.array_equal(o_b, wl.to_bf16_bits(o_w))
+    assert np.array_equal(s_b, s_w) and np.array_equal(i_b, i_w)
+
+
 def pin_golden_hand():
     """tests/golden/hand_k2_v2.json: a two-token example worked by hand in exact
     dyadic arithmetic."""
@@ -498,5 +524,5 @@ def pin_bf16_rounding():
 ALL_PINS = [pin_dense_fp64, pin_dense_unrolled, pin_beta_zero_decay_only, pin_delta_retrieval,
             pin_scalar_state, pin_gather_probe, pin_scatter_probe, pin_linearity_pow2,
             pin_verify_fold_identities, pin_replicated_heads, pin_fused_matches_packed,
-            pin_snapshots, pin_snapshot_rollback, pin_per_v_beta, pin_bf16_ring, pin_golden_hand,
-            pin_bf16_rounding]
+            pin_snapshots, pin_snapshot_rollback, pin_per_v_beta, pin_bf16_ring, pin_bf16_work,
+            pin_golden_hand, pin_bf16_rounding]

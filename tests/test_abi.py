@@ -87,6 +87,10 @@ def call_fwd(a, nv=4, nk=2):
     (dict(qkv=T([10, 128], stride=[256, 2])), -2),                  # innermost stride
     (dict(qkv=T([10, 128], data=FAKE + 4)), -2),                   # misaligned base
     (dict(state=T([6, 4, 16, 16], B.GDR_DTYPE_BF16, stride=[1024, 256, 17, 1])), -2),
+    (dict(qkv=T([10, 128], B.GDR_DTYPE_BF16)), -2),               # work dtypes differ
+    (dict(out=T([10, 64], B.GDR_DTYPE_BF16)), -2),                # output not the work dtype
+    (dict(qkv=T([10, 128], B.GDR_DTYPE_BF16, stride=[132, 1]), decay=T([10, 4], B.GDR_DTYPE_BF16),
+          beta=T([10, 4], B.GDR_DTYPE_BF16), out=T([10, 64], B.GDR_DTYPE_BF16)), -2),  # bf16 rows
 ])
 def test_fwd_rejects_bad_arguments(case, code):
     rc = call_fwd(fwd_args(**case))
@@ -154,6 +158,7 @@ def test_fused_argument_checks():
     assert call(beta=T([2, 3, 4, 8])) == -1                        # per-V beta must match v
     assert call(beta=T([2, 3, 4, 16], stride=[192, 64, 1, 4])) == -2  # V axis not unit stride
     assert call(v=T([2, 3, 4, 32]), o=T([2, 3, 4, 32])) == -2      # K != V
+    assert call(v=T([2, 3, 4, 16], B.GDR_DTYPE_BF16)) == -2        # work dtypes differ
     st = T([5, 4, 16, 16], B.GDR_DTYPE_BF16)
     assert call(state=st, inter=T([5, 3, 4, 16, 16], B.GDR_DTYPE_F32)) == -2  # dtype mismatch
     assert call(state=st, idx=T([3], B.GDR_DTYPE_I32)) == -1       # indices must be [N]

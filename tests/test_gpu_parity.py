@@ -544,3 +544,70 @@ def test_bf16_ring_verify_and_fold():
     ties = H.assert_state_close(fold_b[sl], fold_r[sl], "bf16-ring fold state", unr_f[sl])
     n_fit = int((lens <= ring_len).sum())
     say(f"bf16 ring: {n_fit} rows folded, fold ties {ties}")
+
+
+# ------------------------------------------------------- bf16 work dtype ---
+
+def _bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _widened(w, keys):
+    return dict(w, **{k: wl.bf16_bits_to_f32(w[k]) for k in keys if w.get(k) is not None})
+
+
+def test_bf16_work_dtype_packed():
+    """bf16 qkv / decay / beta / output (verify page, work_dtype) through the
+    forward and the verify: against the oracle (outputs within tolerance or a
+    bf16 rounding tie of the oracle's unrounded output), and on the GPU bit for
+    bit the float32 path on the widened inputs with its output rounded once."""
+    import torch
+    keys = ("qkv", "decay", "beta")
+    w = wl.bf16_work(wl.decode_step(batch=96, slots=128))
+    ww = _widened(w, keys)
+    say("bf16 work: decode step B=96")
+    out_b, st_b = H.gpu_fwd(w)
+    out_w, st_w = H.gpu_fwd(ww)
+    assert out_b.dtype == np.uint16
+    want = torch.from_numpy(out_w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out_b, want), "bf16 output != rounded float32-path output"
+    assert np.array_equal(st_b, st_w)
+    out_r, st_r = oracle_fwd(w)
+    out_u, _ = oracle_fwd(ww)
+    ties = H.assert_state_close(out_b, out_r, "bf16 work output", out_u)
+    sl = touched(w)
+    _, unr = oracle_fwd(w, state=H.f32_pool(w["state"]))
+    ties += H.assert_state_close(st_b[sl], st_r[sl], "bf16 work state", unr[sl])
+    # verify with bf16 work: output == forward output, ring == float32 path's
+    v = wl.bf16_work(wl.verify_window())
+    vw = _widened(v, keys)
+    o_vb, s_vb, r_vb = H.gpu_verify(v)
+    o_vw, s_vw, r_vw = H.gpu_verify(vw)
+    o_fb, _ = H.gpu_fwd(v)
+    assert np.array_equal(o_vb, o_fb), "bf16 verify output != bf16 forward output"
+    assert np.array_equal(_bits(r_vb), _bits(r_vw)) and np.array_equal(s_vb, s_vw)
+    want = torch.from_numpy(o_vw).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o_vb, want)
+    say(f"bf16 work packed: ties {ties}")
+
+
+def test_bf16_work_dtype_fused():
+    """Fused update with bf16 q, k, v, g, beta and o: GPU == float32 path on
+    the widened inputs (output rounded once), and the oracle within tolerance."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(95))
+    w = wl.bf16_work(wl.gdp_inputs(rng, B=24, S_draft=4, M=2, H=4, HV=8, K=128, V=128,
+                                   slots=30, pad_frac=0.1, state_sigma=0.05))
+    ww = _widened(w, ("q", "k", "v", "g", "beta"))
+    say("bf16 work: fused B=24 T=8 spt=2")
+    o_b, st_b, i_b = H.gpu_fused(w)
+    o_w, st_w, i_w = H.gpu_fused(ww)
+    assert o_b.dtype == np.uint16
+    want = torch.from_numpy(o_w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o_b, want)
+    assert np.array_equal(st_b, st_w) and np.array_equal(i_b, i_w)
+    o_r, st_r, _ = fused_oracle(w)
+    o_u, _, _ = fused_oracle(ww)
+    ties = H.assert_state_close(o_b, o_r, "bf16 work fused output", o_u)
+    say(f"bf16 work fused: ties {ties}")
