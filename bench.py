@@ -1,7 +1,8 @@
 """Benchmark of the gated delta rule recurrence on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--only decode,decode_bf16,prefill,verify,gdp]
+                    [--only decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,
+                            gdp_v256,gdp_betacols]
                     [--no-cpu-baseline] [--copy-probe MiB]
 
 Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
@@ -14,9 +15,10 @@ region on the stream the kernels run on, divided by the launch count.
 
 Also timed (reported under "configs"): the decode step with bf16 per-token
 inputs and output, the ragged prefill (VALU-bound), the speculative verify +
-fold (HBM-bound) and the Gated DeltaProduct decode with snapshots and the
-snapshot rollback (HBM-bound).  The CPU baseline is the plain C oracle timed on the
-host on a bounded sample of the decode workload.
+fold with a float32 and with a bf16 ring (HBM-bound), the Gated DeltaProduct
+decode with snapshots and the snapshot rollback (HBM-bound), and that decode
+with V = 256 (K != V) and with per-column beta.  The CPU baseline is the
+plain C oracle timed on the host on a bounded sample of the decode workload.
 """
 from __future__ import annotations
 
@@ -164,8 +166,13 @@ def case_prefill(torch, gdr, B, wl, rotations):
                 extra={"max_len": int(lens.max()), "lengths": lens.tolist()})
 
 
-def case_verify_fold(torch, gdr, B, wl, rotations):
+def case_verify_fold(torch, gdr, B, wl, rotations, ring_bf16=False):
     w = wl.verify_window()
+    suffix = ""
+    if ring_bf16:  # the same window with a bf16 ring (verify page, ring_dtype)
+        w = dict(w, ring=np.zeros(w["ring"].shape, np.uint16))
+        suffix = "_bf16ring"
+    ring_es = 2 if ring_bf16 else 4
     lens = np.diff(w["row_offsets"].astype(np.int64))
     ring_len = w["ring"].shape[2]
     verifies, folds = [], []
@@ -189,27 +196,36 @@ def case_verify_fold(torch, gdr, B, wl, rotations):
     T = int(lens.sum())
     long_rows = lens > ring_len
     state_v = 64 * nv * head + int(long_rows.sum()) * nv * head
-    ring_w = int(lens[~long_rows].sum()) * nk * rec * 4
+    ring_w = int(lens[~long_rows].sum()) * nk * rec * ring_es
     alg_v = state_v + ring_w + w["qkv"].nbytes + T * nv * V * 4 + 2 * T * nv * 4
     acc = w["accepted"].astype(np.int64)
     fold_rows = (acc > 0) & (acc <= ring_len)
     state_f = int(fold_rows.sum()) * nv * head * 2
-    alg_f = state_f + int(acc[fold_rows].sum()) * nk * rec * 4
-    cv = Case("verify_64x12", verifies, alg_v, state_v + ring_w, T,
+    alg_f = state_f + int(acc[fold_rows].sum()) * nk * rec * ring_es
+    cv = Case("verify_64x12" + suffix, verifies, alg_v, state_v + ring_w, T,
               FLOPS_PER_TOKEN_HEAD_ELEM * T * nv * K * V,
               extra={"long_rows": int(long_rows.sum())})
-    cf = Case("fold_64x12", folds, alg_f, state_f, int(acc[fold_rows].sum()),
+    cf = Case("fold_64x12" + suffix, folds, alg_f, state_f, int(acc[fold_rows].sum()),
               2 * 2 * int(acc[fold_rows].sum()) * nv * K * V,
               extra={"folded_rows": int(fold_rows.sum())})
     return cv, cf
 
 
-def case_gdp(torch, gdr, B, wl, rotations):
+def case_gdp(torch, gdr, B, wl, rotations, V=128, beta_cols=False):
+    """GDP decode (B=128, 4 drafts x 2 copies, H=16, HV=32, K=128) and the
+    rollback after it; variants: value head dim V (K != V) or per-column beta
+    (those return the decode case only)."""
     launches = []
     rb_sets = []
     w0 = None
+    variant = V != 128 or beta_cols
     for r in range(rotations):
-        w = wl.gdp_decode(seed=1004 + 100 * r)
+        if variant:
+            rng = np.random.Generator(np.random.PCG64(1004 + 100 * r))
+            w = wl.gdp_inputs(rng, B=128, S_draft=4, M=2, H=16, HV=32, K=128, V=V, slots=160,
+                              pad_frac=0.1, state_sigma=0.05, beta_per_v=beta_cols)
+        else:
+            w = wl.gdp_decode(seed=1004 + 100 * r)
         w0 = w0 or w
         t = {k: _dev(torch, w[k]) for k in ("q", "k", "v", "g", "beta", "state",
                                            "intermediate_states")}
@@ -245,14 +261,18 @@ def case_gdp(torch, gdr, B, wl, rotations):
             assert rc == 0, B.gdr_last_error_message()
         rb_launches.append(rollback)
     rolled = int(((idx >= 0) & (acc >= 1) & (acc <= 4)).sum())
-    HV, H, K, V, T = 32, 16, 128, 128, 8
+    HV, H, K, T = 32, 16, 128, 8
     head = K * V * 2
     state = act * HV * head * 2 + act * HV * head * (T // 2)
-    inputs = act * T * (2 * H * K + HV * V + 2 * HV) * 4
+    beta_elems = HV * V if beta_cols else HV
+    inputs = act * T * (2 * H * K + HV * V + HV + beta_elems) * 4
     outs = 128 * T * HV * V * 4
-    gdp = Case("gdp_128x8", launches, state + inputs + outs, state, act * T,
+    name = "gdp_128x8" + (f"_K128V{V}" if V != 128 else "") + ("_betacols" if beta_cols else "")
+    gdp = Case(name, launches, state + inputs + outs, state, act * T,
                FLOPS_PER_TOKEN_HEAD_ELEM * act * T * HV * K * V,
                extra={"active_rows": act, "draft_tokens": act * T // 2})
+    if variant:
+        return (gdp,)
     rb_bytes = rolled * HV * head * 2
     rb = Case("rollback_128x4", rb_launches, rb_bytes, rb_bytes, rolled,
               extra={"rolled_rows": rolled})
@@ -333,7 +353,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotations", type=int, default=4)
-    ap.add_argument("--only", default="decode,decode_bf16,prefill,verify,gdp")
+    ap.add_argument("--only", default="decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,"
+                                      "gdp_v256,gdp_betacols")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -361,8 +382,14 @@ def main():
         cases.append(case_prefill(torch, gdr, B, wl, 2))
     if "verify" in only:
         cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations))
+    if "verify_bf16ring" in only:
+        cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations, ring_bf16=True))
     if "gdp" in only:
         cases.extend(case_gdp(torch, gdr, B, wl, 2))
+    if "gdp_v256" in only:
+        cases.extend(case_gdp(torch, gdr, B, wl, 2, V=256))
+    if "gdp_betacols" in only:
+        cases.extend(case_gdp(torch, gdr, B, wl, 2, beta_cols=True))
     torch.cuda.synchronize()
 
     results = {}

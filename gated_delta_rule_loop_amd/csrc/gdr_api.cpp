@@ -94,18 +94,32 @@ int check_work_dtype(const char* fn, const char* name, const gdr_tensor* t, int3
 // Outer-stride multiple (in elements) that keeps 16-byte rows for a dtype.
 int64_t vec_mult(int32_t dtype) { return dtype == GDR_DTYPE_BF16 ? 8 : 4; }
 
-bool head_dim_built(int64_t K) { return K == 16 || K == 32 || K == 64 || K == 128; }
+bool head_dim_built(int64_t K) {
+    return K == 16 || K == 32 || K == 64 || K == 128 || K == 256;
+}
+
+// Key/value head dims with kernels: K == V in 16..256, and for the fused
+// update (K != V) the pairs below.
+bool dims_built(int64_t K, int64_t V, bool allow_kv_differ) {
+    if (K == V) return head_dim_built(K);
+    if (!allow_kv_differ) return false;
+    return (K == 64 && V == 128) || (K == 128 && V == 64) || (K == 128 && V == 256) ||
+           (K == 256 && V == 128);
+}
+const char* kDimsBuilt = "K == V in {16, 32, 64, 128, 256}; fused update also (K, V) in "
+                         "{(64, 128), (128, 64), (128, 256), (256, 128)}";
 
 // State-like tensor [slots, nv, K, V] with a dense K x V block per head.
 int check_state(const char* fn, const char* name, const gdr_tensor* t, int ndim,
-                const int64_t* shape) {
+                const int64_t* shape, bool allow_kv_differ = false) {
     int rc = check_tensor(fn, name, t, ndim, shape, true, true, false);
     if (rc) return rc;
     const int64_t K = t->shape[ndim - 2], V = t->shape[ndim - 1];
-    if (K != V) return fail(GDR_ERR_UNSUPPORTED, "%s: %s needs K == V", fn, name);
-    if (!head_dim_built(K))
-        return fail(GDR_ERR_UNSUPPORTED, "%s: head dim %lld not built (16, 32, 64, 128)", fn,
-                    static_cast<long long>(K));
+    if (K != V && !allow_kv_differ)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: %s needs K == V", fn, name);
+    if (!dims_built(K, V, allow_kv_differ))
+        return fail(GDR_ERR_UNSUPPORTED, "%s: head dims K=%lld V=%lld not built (%s)", fn,
+                    static_cast<long long>(K), static_cast<long long>(V), kDimsBuilt);
     if (t->stride[ndim - 1] != 1 || t->stride[ndim - 2] != V)
         return fail(GDR_ERR_UNSUPPORTED, "%s: %s needs a dense K x V block per head", fn, name);
     return check_layout(fn, name, t, t->dtype == GDR_DTYPE_BF16 ? 8 : 4);
@@ -124,12 +138,23 @@ float resolve_scale(float scale, int64_t K) {
 // not depend on this choice.
 enum class Entry { Packed, Fused, Fold };
 
-gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t G, int64_t total_tokens, int64_t rows) {
+gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t total_tokens,
+                            int64_t rows) {
     gdr::LaunchShape s{};
     s.K = static_cast<int>(K);
+    s.V = static_cast<int>(V);
     const bool long_rows = rows > 0 && total_tokens >= 16 * rows;
     const bool decode = rows > 0 && 2 * total_tokens <= 3 * rows;  // ~1 token per row
-    if (K == 128) {
+    if (K == 256 || K != V) {  // one short and one long-row shape per pair
+        if (e == Entry::Fold || !long_rows) {
+            s.cpl = K == 256 ? 2 : (K == 64 ? 8 : 4);
+            s.chunk = e == Entry::Fold ? 1 : 8;
+        } else {
+            s.cpl = K == 64 ? 2 : 1;
+            s.chunk = K == 256 ? 8 : 16;
+            s.kg_low = true;
+        }
+    } else if (K == 128) {
         if (e == Entry::Fold) {
             s.cpl = GDR_FOLD_CPL;
             s.chunk = 1;
@@ -158,7 +183,7 @@ gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t G, int64_t total_tokens,
         s.cpl = K == 64 ? 8 : (K == 32 ? 4 : 2);
         s.chunk = 8;
     }
-    const int64_t tiles = K / (gdr::kLanesPerRow * s.cpl);
+    const int64_t tiles = V / (gdr::kLanesPerRow * s.cpl);
     const int64_t units = G * tiles;
     s.wpg = units % 4 == 0 ? 4 : (units % 2 == 0 ? 2 : 1);
     return s;
@@ -248,8 +273,8 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     if (B * nk > (int64_t{1} << 28))
         return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
 
-    const gdr::LaunchShape s = pick_shape(Entry::Packed, K, G, T, B);
-    const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
+    const gdr::LaunchShape s = pick_shape(Entry::Packed, K, V, G, T, B);
+    const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     p.rows = static_cast<int32_t>(B);
     p.nv = nv;
     p.nk = nk;
@@ -357,8 +382,8 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
         g_last_error.clear();
         return GDR_OK;
     }
-    gdr::LaunchShape s = pick_shape(Entry::Fold, K, G, B, B);
-    const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
+    gdr::LaunchShape s = pick_shape(Entry::Fold, K, V, G, B, B);
+    const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     gdr::FoldParams p{};
     p.rows = static_cast<int32_t>(B);
     p.nv = nv;
@@ -407,10 +432,9 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
         return fail(GDR_ERR_INVALID_ARG, "%s: v must be [B, T, HV, V] like q", fn);
     if (H < 1 || HV < H || HV % H != 0)
         return fail(GDR_ERR_INVALID_ARG, "%s: HV must be a positive multiple of H", fn);
-    if (K != V) return fail(GDR_ERR_UNSUPPORTED, "%s: K != V is not built", fn);
-    if (!head_dim_built(K))
-        return fail(GDR_ERR_UNSUPPORTED, "%s: head dim %lld not built (16, 32, 64, 128)", fn,
-                    static_cast<long long>(K));
+    if (!dims_built(K, V, true))
+        return fail(GDR_ERR_UNSUPPORTED, "%s: head dims K=%lld V=%lld not built (%s)", fn,
+                    static_cast<long long>(K), static_cast<long long>(V), kDimsBuilt);
     if ((rc = check_layout(fn, "q", q, 1)) || (rc = check_layout(fn, "k", k, 1)) ||
         (rc = check_layout(fn, "v", v, vec_mult(work))))
         return rc;
@@ -449,7 +473,7 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     int32_t st_dtype = -1;
     if (present(state)) {
         const int64_t sshape[4] = {-1, HV, K, V};
-        if ((rc = check_state(fn, "state", state, 4, sshape))) return rc;
+        if ((rc = check_state(fn, "state", state, 4, sshape, true))) return rc;
         st_dtype = state->dtype;
         p.src = p.dst = state->data;
         p.src_slot = p.dst_slot = state->stride[0];
@@ -463,7 +487,7 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
         }
         if (present(intermediate_states)) {
             const int64_t ishape[5] = {state->shape[0], -1, HV, K, V};
-            if ((rc = check_state(fn, "intermediate_states", intermediate_states, 5, ishape)))
+            if ((rc = check_state(fn, "intermediate_states", intermediate_states, 5, ishape, true)))
                 return rc;
             if (intermediate_states->dtype != st_dtype)
                 return fail(GDR_ERR_UNSUPPORTED, "%s: intermediate_states must match the state "
@@ -479,14 +503,14 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
             return fail(GDR_ERR_INVALID_ARG, "%s: intermediate_states needs state", fn);
         const int64_t dshape[4] = {N, HV, K, V};
         if (present(initial_state)) {
-            if ((rc = check_state(fn, "initial_state", initial_state, 4, dshape))) return rc;
+            if ((rc = check_state(fn, "initial_state", initial_state, 4, dshape, true))) return rc;
             st_dtype = initial_state->dtype;
             p.src = initial_state->data;
             p.src_slot = initial_state->stride[0];
             p.src_head = initial_state->stride[1];
         }
         if (present(final_state)) {
-            if ((rc = check_state(fn, "final_state", final_state, 4, dshape))) return rc;
+            if ((rc = check_state(fn, "final_state", final_state, 4, dshape, true))) return rc;
             if (st_dtype >= 0 && final_state->dtype != st_dtype)
                 return fail(GDR_ERR_UNSUPPORTED, "%s: initial and final state dtypes differ", fn);
             st_dtype = final_state->dtype;
@@ -502,8 +526,8 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     if (N * H > (int64_t{1} << 28)) return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
 
     const int64_t G = HV / H;
-    const gdr::LaunchShape s = pick_shape(Entry::Fused, K, G, B * T, N);
-    const int64_t units = G * (K / (gdr::kLanesPerRow * s.cpl));
+    const gdr::LaunchShape s = pick_shape(Entry::Fused, K, V, G, B * T, N);
+    const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     p.rows = static_cast<int32_t>(N);
     p.nv = static_cast<int32_t>(HV);
     p.nk = static_cast<int32_t>(H);
@@ -543,11 +567,12 @@ int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indic
                           void* stream) {
     const char* fn = "gdr_snapshot_rollback";
     int rc;
-    if ((rc = check_state(fn, "state", state, 4, nullptr))) return rc;
+    if ((rc = check_state(fn, "state", state, 4, nullptr, true))) return rc;
     const int64_t S = state->shape[0], HV = state->shape[1], K = state->shape[2],
                   V = state->shape[3];
     const int64_t ishape[5] = {S, -1, HV, K, V};
-    if ((rc = check_state(fn, "intermediate_states", intermediate_states, 5, ishape))) return rc;
+    if ((rc = check_state(fn, "intermediate_states", intermediate_states, 5, ishape, true)))
+        return rc;
     if (intermediate_states->dtype != state->dtype)
         return fail(GDR_ERR_UNSUPPORTED, "%s: intermediate_states must match the state dtype", fn);
     if (!present(state_indices)) return fail(GDR_ERR_INVALID_ARG, "%s: state_indices is null", fn);

@@ -256,9 +256,8 @@ __device__ __forceinline__ float widen_raw(float raw) {
 
 // ST: state storage type; WT: per-token input/output type (float, or
 // uint16_t holding bf16 bits).  Arithmetic is float32 either way.
-template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT>
+template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT>
 struct Rec {
-    static constexpr int V = K;
     static constexpr int R = K / kRowGroups;
     static constexpr int BV = kLanesPerRow * CPL;
     static constexpr int TILES = V / BV;
@@ -638,9 +637,9 @@ struct Rec {
 template <int C>
 constexpr int kMinWaves = C == 1 ? 4 : 1;
 
-template <int K, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
+template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
 __global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecParams p) {
-    using Q = Rec<K, CPL, C, WPG, ST, KG_LOW, WT>;
+    using Q = Rec<K, V, CPL, C, WPG, ST, KG_LOW, WT>;
     __shared__ __attribute__((aligned(16))) float lds[2 * Q::template buf<(MODE & kBetaCols) != 0>()];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -664,18 +663,18 @@ __global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecPa
 
 }  // namespace
 
-template <int K, int CPL, int C, typename ST, bool KG_LOW, typename WT, int MODE>
+template <int K, int V, int CPL, int C, typename ST, bool KG_LOW, typename WT, int MODE>
 static hipError_t launch_rec_mode(const RecParams& p, int wpg, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(p.rows) * p.nk * p.parts);
-    constexpr int TILES = K / (kLanesPerRow * CPL);
+    constexpr int TILES = V / (kLanesPerRow * CPL);
     if constexpr (TILES % 4 == 0) {  // every head splits into a multiple of 4 waves
         if (wpg != 4) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, WT, MODE>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((rec_kernel<K, V, CPL, C, 4, ST, KG_LOW, WT, MODE>), grid, dim3(256), 0, stream, p);
     } else {
         switch (wpg) {
-            case 1: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 1, ST, KG_LOW, WT, MODE>), grid, dim3(64), 0, stream, p); break;
-            case 2: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 2, ST, KG_LOW, WT, MODE>), grid, dim3(128), 0, stream, p); break;
-            case 4: hipLaunchKernelGGL((rec_kernel<K, CPL, C, 4, ST, KG_LOW, WT, MODE>), grid, dim3(256), 0, stream, p); break;
+            case 1: hipLaunchKernelGGL((rec_kernel<K, V, CPL, C, 1, ST, KG_LOW, WT, MODE>), grid, dim3(64), 0, stream, p); break;
+            case 2: hipLaunchKernelGGL((rec_kernel<K, V, CPL, C, 2, ST, KG_LOW, WT, MODE>), grid, dim3(128), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL((rec_kernel<K, V, CPL, C, 4, ST, KG_LOW, WT, MODE>), grid, dim3(256), 0, stream, p); break;
             default: return hipErrorInvalidValue;
         }
     }
@@ -687,20 +686,32 @@ static hipError_t launch_rec_mode(const RecParams& p, int wpg, hipStream_t strea
 // so the library compiles in parallel.
 template <typename WT, typename ST, int MODE>
 hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_t stream) {
-#define GDR_REC_CASE(KK, CC, CH, KL)                                              \
-    if (s.K == KK && s.cpl == CC && s.chunk == CH && s.kg_low == KL)             \
-        return launch_rec_mode<KK, CC, CH, ST, KL, WT, MODE>(p, s.wpg, stream);
-    GDR_REC_CASE(128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
-    GDR_REC_CASE(128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
-    GDR_REC_CASE(128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
-    GDR_REC_CASE(128, GDR_LONG_CPL, GDR_LONG_CHUNK, GDR_LONG_KGLOW)
+#define GDR_REC_CASE(KK, VV, CC, CH, KL)                                              \
+    if (s.K == KK && s.V == VV && s.cpl == CC && s.chunk == CH && s.kg_low == KL)    \
+        return launch_rec_mode<KK, VV, CC, CH, ST, KL, WT, MODE>(p, s.wpg, stream);
+    GDR_REC_CASE(128, 128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
+    GDR_REC_CASE(128, 128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
+    GDR_REC_CASE(128, 128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
+    GDR_REC_CASE(128, 128, GDR_LONG_CPL, GDR_LONG_CHUNK, GDR_LONG_KGLOW)
 #ifndef GDR_ONLY_K128
-    GDR_REC_CASE(64, 8, 8, false)
-    GDR_REC_CASE(64, 2, 16, true)
-    GDR_REC_CASE(32, 4, 8, false)
-    GDR_REC_CASE(32, 2, 16, true)
-    GDR_REC_CASE(16, 2, 8, false)
-    GDR_REC_CASE(16, 2, 16, true)
+    GDR_REC_CASE(256, 256, 2, 8, false)
+    GDR_REC_CASE(256, 256, 1, 8, true)
+    GDR_REC_CASE(64, 64, 8, 8, false)
+    GDR_REC_CASE(64, 64, 2, 16, true)
+    GDR_REC_CASE(32, 32, 4, 8, false)
+    GDR_REC_CASE(32, 32, 2, 16, true)
+    GDR_REC_CASE(16, 16, 2, 8, false)
+    GDR_REC_CASE(16, 16, 2, 16, true)
+    if constexpr ((MODE & 3) != kVerify) {  // K != V: the fused update only
+        GDR_REC_CASE(64, 128, 8, 8, false)
+        GDR_REC_CASE(64, 128, 2, 16, true)
+        GDR_REC_CASE(128, 64, 4, 8, false)
+        GDR_REC_CASE(128, 64, 1, 16, true)
+        GDR_REC_CASE(128, 256, 4, 8, false)
+        GDR_REC_CASE(128, 256, 1, 16, true)
+        GDR_REC_CASE(256, 128, 2, 8, false)
+        GDR_REC_CASE(256, 128, 1, 8, true)
+    }
 #endif
 #undef GDR_REC_CASE
     return hipErrorInvalidValue;

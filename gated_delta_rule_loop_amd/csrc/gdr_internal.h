@@ -69,7 +69,7 @@ enum class StateType { F32 = 0, BF16 = 1 };
 
 // Launch configuration picked by the host for one call.
 struct LaunchShape {
-    int K;          // == V
+    int K, V;       // key and value head dims
     int cpl;        // value columns per lane (8 lanes share one key-row group)
     int chunk;      // tokens staged per barrier
     int wpg;        // waves per workgroup

@@ -322,10 +322,11 @@ def test_launch_shape_independence():
     assert np.array_equal(st_a[s], st_b[s])
 
 
-def test_fold_equals_forward_prefix_every_n():
+@pytest.mark.parametrize("K", [128, 256])
+def test_fold_equals_forward_prefix_every_n(K):
     ring_len = 6
     lengths = [1, 6, 3, 9, 5]
-    nk, nv, K, V = 2, 4, 128, 128
+    nk, nv, V = 2, 4, K
     w = P.small_packed(40, lengths, nk=nk, nv=nv, K=K, V=V, slots=7, state_dtype="bf16")
     stride = wl.ring_record_stride(nv // nk, K, V)
     w["ring"] = np.zeros((5, nk, ring_len, stride), np.float32)
@@ -347,9 +348,9 @@ def test_fold_equals_forward_prefix_every_n():
 
 # ------------------------------------------------------------ edge cases ---
 
-@pytest.mark.parametrize("K", [16, 32, 64, 128])
+@pytest.mark.parametrize("K", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("state_dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("lengths", [[0, 3, 1, 7], [25, 0, 19]])
+@pytest.mark.parametrize("lengths", [[0, 3, 1, 7], [25, 0, 19], [40, 0, 33]])
 def test_small_shapes(K, state_dtype, lengths):
     say(f"small shapes K={K} {state_dtype} lengths {lengths}")
     w = P.small_packed(50 + K, lengths, nk=2, nv=4, K=K, V=K, slots=5, state_dtype=state_dtype,
@@ -611,3 +612,29 @@ def test_bf16_work_dtype_fused():
     o_u, _, _ = fused_oracle(ww)
     ties = H.assert_state_close(o_b, o_r, "bf16 work fused output", o_u)
     say(f"bf16 work fused: ties {ties}")
+
+
+# ------------------------------------------------------- head dims, K != V ---
+
+@pytest.mark.parametrize("K,V", [(256, 256), (64, 128), (128, 64), (128, 256), (256, 128)])
+@pytest.mark.parametrize("S_draft", [3, 20])
+def test_fused_head_dims(K, V, S_draft):
+    """Fused update at the other built head dims (K != V included), short
+    rows and long rows (the two launch shapes), bf16 cache with snapshots:
+    against the oracle; last snapshot == final state bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(300 + K + V + S_draft))
+    w = wl.gdp_inputs(rng, B=6, S_draft=S_draft, M=2, H=2, HV=4, K=K, V=V, slots=9,
+                      pad_frac=0.2, state_sigma=0.05)
+    say(f"fused head dims K={K} V={V} T={2 * S_draft}")
+    o_g, st_g, inter_g = H.gpu_fused(w)
+    o_r, st_r, inter_r = fused_oracle(w)
+    _, st_u, inter_u = fused_oracle(w, f32=True)
+    err = H.assert_close(o_g, o_r, f"K{K}V{V} output")
+    idx = w["state_indices"]
+    sl = idx[idx >= 0].astype(np.int64)
+    ties = H.assert_state_close(st_g[sl], st_r[sl], f"K{K}V{V} state", st_u[sl])
+    ties += H.assert_state_close(inter_g[sl], inter_r[sl], f"K{K}V{V} snapshots", inter_u[sl])
+    assert np.array_equal(inter_g[sl, -1], st_g[sl])
+    others = np.setdiff1d(np.arange(9), sl)
+    assert np.array_equal(st_g[others], w["state"][others])
+    say(f"K{K}V{V}: out rel err {err:.2e}, ties {ties}")
