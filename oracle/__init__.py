@@ -35,7 +35,7 @@ def _load():
         _lib = ctypes.CDLL(_LIB_PATH)
         for name in ("oracle_recurrence_fwd", "oracle_recurrence_verify_ring",
                      "oracle_state_fold", "oracle_fused_recurrent_update",
-                     "oracle_snapshot_rollback"):
+                     "oracle_snapshot_rollback", "oracle_causal_conv1d"):
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
 
@@ -53,7 +53,7 @@ class using_library:
         lib = ctypes.CDLL(self.path)
         for name in ("oracle_recurrence_fwd", "oracle_recurrence_verify_ring",
                      "oracle_state_fold", "oracle_fused_recurrent_update",
-                     "oracle_snapshot_rollback"):
+                     "oracle_snapshot_rollback", "oracle_causal_conv1d"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -263,6 +263,39 @@ def snapshot_rollback(*, state, state_indices, intermediate_states, accepted):
     if rc != 0:
         raise ValueError(f"oracle_snapshot_rollback failed: {rc}")
     return st
+
+
+def causal_conv1d(*, x, weight, slot_idx, row_offsets, bias=None, conv_state=None,
+                  silu=False):
+    """Pass-1 causal depthwise Conv1d producing qkv_conv_output (named on the
+    "gated_delta_recurrence_fwd_gpu" page; the reading is stated in
+    gdr_oracle.c).  x [T, C] float32 or uint16 (bf16 bits: the work dtype,
+    whose output is rounded once); weight [C, W] and bias [C] float32;
+    conv_state [slots, W-1, C] of x's dtype, or None (zero history, not
+    updated), copied.  Returns (out [T, C] of x's dtype, conv_state_after)."""
+    lib = _load()
+    (xf,), bf = _work((x,))
+    st = None
+    if conv_state is not None:
+        (st,), sbf = _work((conv_state,))
+        if sbf != bf:
+            raise TypeError("conv_state must have x's dtype")
+        st = np.array(st, dtype=np.float32, order="C", copy=True)
+    w = np.ascontiguousarray(weight, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    off = np.ascontiguousarray(row_offsets, dtype=np.uint32)
+    sl = np.ascontiguousarray(slot_idx, dtype=np.uint32)
+    T, C = xf.shape
+    W = w.shape[1]
+    out = np.zeros((T, C), dtype=np.float32)
+    rc = lib.oracle_causal_conv1d(
+        sl.shape[0], C, W, _p(off), _p(sl), _p(xf), _p(w), _p(b), _p(st),
+        ctypes.c_int64(0 if st is None else st.shape[0]), int(silu), _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle_causal_conv1d failed: {rc}")
+    if bf:
+        return bf16_round(out), (None if st is None else bf16_round(st))
+    return out, st
 
 
 def fwd_output_shape(qkv_shape, state_shape):

@@ -16,6 +16,8 @@
  *   [gdp]    "core.ssm.ops.gdp.fused_recurrent" (Megatron Core API page):
  *            module summary, fused_recurrent_gated_delta_rule_update
  *            parameters.
+ * The Pass-1 causal Conv1d that produces the fwd page's qkv_conv_output is
+ * only named there; oracle_causal_conv1d states the reading it implements.
  *
  * The recurrence (per sequence and value head, a K x V state S carried token
  * by token; the pages call it the gated delta rule and describe the state as
@@ -506,5 +508,91 @@ int oracle_snapshot_rollback(int N, int HV, int K, int V, int elem_size, void* s
         for (int64_t b = 0; b < block; ++b)
             dst[b] = src[b];
     }
+    return 0;
+}
+
+/* ---------------------------------------------- Pass-1 causal Conv1d ------ */
+
+/*
+ * [fwd] Args, qkv_conv_output: the recurrence consumes the output of a
+ * Conv1d "Pass 1" that the pages name but do not specify.  Reading used here
+ * (the plainest one the name and the packed layout support): a causal,
+ * depthwise (one filter per channel) convolution along the token axis of each
+ * ragged row, of width W, plus an optional per-channel bias, optionally
+ * followed by SiLU, y * sigmoid(y).  Each row continues the history of its
+ * slot: the W-1 inputs before the row's first token come from conv_state
+ * (zeros when conv_state is NULL), and after the row the slot's conv_state
+ * holds the last W-1 inputs of history ++ row.
+ *
+ *   x, out      [T, C] (out written for every token of every row)
+ *   weight      [C, W]: tap j multiplies the input W-1-j tokens back
+ *   bias        [C] or NULL
+ *   conv_state  [num_slots, W-1, C] or NULL; entry i holds the input at
+ *               relative position i - (W-1) before the row (i = W-2 is the
+ *               most recent)
+ *   slot_idx    [B] (0xFFFFFFFF = padding: zero output, nothing touched)
+ *   row_offsets [B+1]
+ * Rows of length 0 leave everything alone.
+ */
+int oracle_causal_conv1d(int B, int C, int W, const uint32_t* row_offsets,
+                         const uint32_t* slot_idx, const float* x, const float* weight,
+                         const float* bias, float* conv_state, int64_t num_slots, int silu,
+                         float* out)
+{
+    const int H = W - 1;
+    float* window = (float*)malloc(sizeof(float) * (size_t)W);
+    for (int b = 0; b < B; ++b) {
+        const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];
+        const uint32_t slot = slot_idx[b];
+        if (slot == ORACLE_PAD_SLOT) {
+            for (int64_t t = t0; t < t1; ++t)
+                for (int c = 0; c < C; ++c)
+                    out[t * C + c] = 0.0f;
+            continue;
+        }
+        if (t1 <= t0)
+            continue;
+        if (conv_state && (int64_t)slot >= num_slots) {
+            free(window);
+            return -2;
+        }
+        for (int c = 0; c < C; ++c) {
+            for (int64_t t = t0; t < t1; ++t) {
+                /* window[j] = input at position t - (W-1) + j */
+                for (int j = 0; j < W; ++j) {
+                    const int64_t s = t - H + j;
+                    if (s >= t0)
+                        window[j] = x[s * C + c];
+                    else if (conv_state)
+                        window[j] = conv_state[((int64_t)slot * H + (H + (s - t0))) * C + c];
+                    else
+                        window[j] = 0.0f;
+                }
+                float y = bias ? bias[c] : 0.0f;
+                for (int j = 0; j < W; ++j)
+                    y = y + weight[(int64_t)c * W + j] * window[j];
+                if (silu)
+                    y = y / (1.0f + expf(-y));
+                out[t * C + c] = y;
+            }
+        }
+        if (conv_state) {
+            /* new history: the last H inputs of old history ++ row */
+            const int64_t L = t1 - t0;
+            for (int c = 0; c < C; ++c) {
+                float* hist = window; /* reuse: H <= W values */
+                for (int i = 0; i < H; ++i) {
+                    const int64_t s = t1 - H + i; /* absolute position */
+                    if (s >= t0)
+                        hist[i] = x[s * C + c];
+                    else
+                        hist[i] = conv_state[((int64_t)slot * H + (L + i)) * C + c];
+                }
+                for (int i = 0; i < H; ++i)
+                    conv_state[((int64_t)slot * H + i) * C + c] = hist[i];
+            }
+        }
+    }
+    free(window);
     return 0;
 }

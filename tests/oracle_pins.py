@@ -488,6 +488,93 @@ def pin_bf16_work():
     assert np.array_equal(s_b, s_w) and np.array_equal(i_b, i_w)
 
 
+def _conv_inputs(seed, lengths, C=6, W=4, slots=5):
+    rng = _rng(seed)
+    T = int(sum(lengths))
+    off = np.zeros(len(lengths) + 1, np.uint32)
+    off[1:] = np.cumsum(lengths)
+    x = rng.standard_normal((T, C)).astype(np.float32)
+    w = rng.standard_normal((C, W)).astype(np.float32)
+    b = rng.standard_normal(C).astype(np.float32)
+    st = rng.standard_normal((slots, W - 1, C)).astype(np.float32)
+    sl = rng.choice(slots, size=len(lengths), replace=False).astype(np.uint32)
+    return dict(x=x, weight=w, bias=b, conv_state=st, slot_idx=sl, row_offsets=off)
+
+
+def pin_conv_taps():
+    """Causal Conv1d reading: a one-hot filter at tap j delays the input by
+    W-1-j tokens, the first ones coming from the slot's history; the new
+    history is the last W-1 inputs of history ++ row."""
+    lengths = [5, 1, 0, 2]
+    W, C = 4, 6
+    a = _conv_inputs(31, lengths, C=C, W=W)
+    off = a["row_offsets"]
+    for j in range(W):
+        w = np.zeros((C, W), np.float32)
+        w[:, j] = 1.0
+        out, st = oracle.causal_conv1d(**dict(a, weight=w, bias=None))
+        d = W - 1 - j
+        for b, L in enumerate(lengths):
+            hist = a["conv_state"][a["slot_idx"][b]]
+            seq = np.concatenate([hist, a["x"][off[b]:off[b + 1]]])
+            for t in range(L):
+                assert np.array_equal(out[off[b] + t], seq[W - 1 + t - d]), (j, b, t)
+            want = seq[-(W - 1):] if L else hist
+            assert np.array_equal(st[a["slot_idx"][b]], want), (j, b)
+
+
+def pin_conv_numpy():
+    """With zero history the output is the per-channel full convolution of the
+    row with the reversed filter, plus bias (numpy's convolve, float64)."""
+    lengths = [7, 3, 12]
+    a = _conv_inputs(32, lengths, W=3)
+    out, _ = oracle.causal_conv1d(**dict(a, conv_state=None))
+    off = a["row_offsets"]
+    for b, L in enumerate(lengths):
+        for c in range(a["x"].shape[1]):
+            xr = a["x"][off[b]:off[b + 1], c].astype(np.float64)
+            want = np.convolve(xr, a["weight"][c, ::-1].astype(np.float64))[:L] + a["bias"][c]
+            _close(out[off[b]:off[b + 1], c], want, 1e-6, f"conv row {b} ch {c}")
+
+
+def pin_conv_continuity():
+    """Splitting every row in two calls (the first updating the history)
+    gives the outputs and history of one call over the whole rows, bit for
+    bit; padding rows give +0.0 and touch nothing; SiLU is y * sigmoid(y)."""
+    lengths = [9, 4, 6]
+    a = _conv_inputs(33, lengths, W=4)
+    off = a["row_offsets"].astype(np.int64)
+    whole, st_whole = oracle.causal_conv1d(**a)
+    cut = [3, 1, 6]
+    for part in (0, 1):
+        rows = [np.arange(off[b], off[b] + cut[b]) if part == 0 else
+                np.arange(off[b] + cut[b], off[b + 1]) for b in range(3)]
+        o2 = np.zeros(len(lengths) + 1, np.uint32)
+        o2[1:] = np.cumsum([len(r) for r in rows])
+        sub = dict(a, x=a["x"][np.concatenate(rows)], row_offsets=o2,
+                   conv_state=a["conv_state"] if part == 0 else st_part)
+        out_p, st_part = oracle.causal_conv1d(**sub)
+        assert np.array_equal(out_p, whole[np.concatenate(rows)]), part
+    assert np.array_equal(st_part, st_whole)
+    pad = dict(a, slot_idx=a["slot_idx"].copy())
+    pad["slot_idx"][1] = 0xFFFFFFFF
+    out_pad, st_pad = oracle.causal_conv1d(**pad)
+    z = out_pad[off[1]:off[2]]
+    assert np.array_equal(z, np.zeros_like(z)) and not np.signbit(z).any()
+    assert np.array_equal(st_pad[a["slot_idx"][1]], a["conv_state"][a["slot_idx"][1]])
+    y, _ = oracle.causal_conv1d(**a)
+    s_, _ = oracle.causal_conv1d(**a, silu=True)
+    y64 = y.astype(np.float64)
+    _close(s_, y64 / (1.0 + np.exp(-y64)), 1e-6, "silu")
+    xb = wl.to_bf16_bits(a["x"])
+    sb = wl.to_bf16_bits(a["conv_state"])
+    ob, stb = oracle.causal_conv1d(**dict(a, x=xb, conv_state=sb))
+    ow, stw = oracle.causal_conv1d(**dict(a, x=wl.bf16_bits_to_f32(xb),
+                                          conv_state=wl.bf16_bits_to_f32(sb)))
+    assert np.array_equal(ob, wl.to_bf16_bits(ow))
+    assert np.array_equal(stb, wl.to_bf16_bits(stw))
+
+
 def pin_golden_hand():
     """tests/golden/hand_k2_v2.json: a two-token example worked by hand in exact
     dyadic arithmetic."""
@@ -525,4 +612,5 @@ ALL_PINS = [pin_dense_fp64, pin_dense_unrolled, pin_beta_zero_decay_only, pin_de
             pin_scalar_state, pin_gather_probe, pin_scatter_probe, pin_linearity_pow2,
             pin_verify_fold_identities, pin_replicated_heads, pin_fused_matches_packed,
             pin_snapshots, pin_snapshot_rollback, pin_per_v_beta, pin_bf16_ring, pin_bf16_work,
-            pin_golden_hand, pin_bf16_rounding]
+            pin_conv_taps, pin_conv_numpy, pin_conv_continuity, pin_golden_hand,
+            pin_bf16_rounding]

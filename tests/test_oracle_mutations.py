@@ -37,6 +37,11 @@ MUTATIONS = [
     ("per_v_beta_ignored", "float b = beta_per_v ? beta[j] : beta[0];", "float b = beta[0];"),
     ("ring_bf16_read_truncated", "return ring_bf16 ? oracle_bf16_widen(((const uint16_t*)ring)[i])",
      "return ring_bf16 ? oracle_bf16_widen(((const uint16_t*)ring)[i] & 0xFF80u)"),
+    ("conv_taps_reversed", "y = y + weight[(int64_t)c * W + j] * window[j];",
+     "y = y + weight[(int64_t)c * W + (W - 1 - j)] * window[j];"),
+    ("conv_history_reversed", "conv_state[((int64_t)slot * H + i) * C + c] = hist[i];",
+     "conv_state[((int64_t)slot * H + i) * C + c] = hist[H - 1 - i];"),
+    ("conv_silu_sign", "y = y / (1.0f + expf(-y));", "y = y / (1.0f + expf(y));"),
     ("offsets_shifted", "const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];",
      "const int64_t t0 = row_offsets[b] + (b > 0), t1 = row_offsets[b + 1];"),
 ]
