@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--only decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,
-                            gdp_v256,gdp_betacols]
+                            gdp_v256,gdp_betacols,conv]
                     [--no-cpu-baseline] [--copy-probe MiB]
 
 Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
@@ -17,8 +17,10 @@ Also timed (reported under "configs"): the decode step with bf16 per-token
 inputs and output, the ragged prefill (VALU-bound), the speculative verify +
 fold with a float32 and with a bf16 ring (HBM-bound), the Gated DeltaProduct
 decode with snapshots and the snapshot rollback (HBM-bound), and that decode
-with V = 256 (K != V) and with per-column beta.  The CPU baseline is the
-plain C oracle timed on the host on a bounded sample of the decode workload.
+with V = 256 (K != V) and with per-column beta; the Pass-1 causal Conv1d over
+the prefill's rows and over a decode step (HBM-bound).  The CPU baseline is
+the plain C oracle timed on the host on a bounded sample of the decode
+workload.
 """
 from __future__ import annotations
 
@@ -148,6 +150,34 @@ def case_decode_bf16(torch, gdr, B, wl, rotations):
     alg = state + Bn * 8192 * 2 + Bn * nv * K * 2 + 2 * Bn * nv * 2 + (2 * Bn + 1) * 4
     flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
     return Case("decode_256x1_bf16io", launches, alg, state, Bn, flops)
+
+
+def case_conv(torch, gdr, B, wl, rotations, decode):
+    """The Pass-1 causal Conv1d (W = 4, bias, SiLU, history) over the prefill's
+    rows or over a decode step's 256 one-token rows; float32 io."""
+    launches = []
+    for r in range(rotations):
+        w = (wl.conv_decode(seed=1006 + 100 * r) if decode
+             else wl.conv_prefill(seed=1005 + 100 * r))
+        t = {k: _dev(torch, w[k]) for k in ("x", "weight", "bias", "conv_state", "slot_idx",
+                                           "row_offsets")}
+        t["out"] = torch.empty_like(t["x"])
+        ds = [B.describe(t[k]) for k in ("out", "x", "weight", "bias", "conv_state", "slot_idx",
+                                         "row_offsets")]
+        refs = [ctypes.byref(d) for d in ds]
+        L = B.lib()
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def launch(refs=refs, st=st, keep=(t, ds)):
+            rc = L.gdr_causal_conv1d(*refs, B.GDR_FLAG_CONV_SILU, st)
+            assert rc == 0, B.gdr_last_error_message()
+        launches.append(launch)
+    T, C = w["x"].shape
+    rows = len(w["slot_idx"])
+    hist = rows * 3 * C * 4 * 2
+    alg = 2 * T * C * 4 + hist + C * 5 * 4
+    name = "conv_decode_256x1" if decode else "conv_prefill_8x4096"
+    return Case(name, launches, alg, hist, T, 2 * 4 * T * C)
 
 
 def case_prefill(torch, gdr, B, wl, rotations):
@@ -354,7 +384,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--only", default="decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,"
-                                      "gdp_v256,gdp_betacols")
+                                      "gdp_v256,gdp_betacols,conv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -382,6 +412,9 @@ def main():
         cases.append(case_prefill(torch, gdr, B, wl, 2))
     if "verify" in only:
         cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations))
+    if "conv" in only:
+        cases.append(case_conv(torch, gdr, B, wl, args.rotations, decode=True))
+        cases.append(case_conv(torch, gdr, B, wl, 2, decode=False))
     if "verify_bf16ring" in only:
         cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations, ring_bf16=True))
     if "gdp" in only:

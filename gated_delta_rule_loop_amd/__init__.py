@@ -7,6 +7,7 @@ library with `python -m gated_delta_rule_loop_amd.build`.
 """
 from ._binding import (  # noqa: F401
     GdrError,
+    gdr_causal_conv1d,
     gdr_fused_recurrent_update,
     gdr_fwd_output_shape,
     gdr_last_error_message,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK = 0
 GDR_DTYPE_F32, GDR_DTYPE_BF16, GDR_DTYPE_U32, GDR_DTYPE_I32 = 0, 1, 2, 3
 GDR_FLAG_L2NORM_QK = 1
+GDR_FLAG_CONV_SILU = 2
 MAX_DIMS = 5
 
 _DTYPES = {torch.float32: GDR_DTYPE_F32, torch.bfloat16: GDR_DTYPE_BF16,
@@ -41,8 +42,9 @@ class GdrError(RuntimeError):
 
 _lib = None
 EXPORTS = ("gdr_recurrence_fwd", "gdr_recurrence_verify_ring", "gdr_state_fold",
-           "gdr_fused_recurrent_update", "gdr_snapshot_rollback", "gdr_fwd_output_shape",
-           "gdr_ring_record_elements", "gdr_last_error_message", "gdr_version")
+           "gdr_fused_recurrent_update", "gdr_snapshot_rollback", "gdr_causal_conv1d",
+           "gdr_fwd_output_shape", "gdr_ring_record_elements", "gdr_last_error_message",
+           "gdr_version")
 
 
 def lib():
@@ -61,12 +63,13 @@ def lib():
         L.gdr_fused_recurrent_update.argtypes = [P, P, P, P, P, f32, P, P, u32, P, P, P, P, i32,
                                                  P, vp]
         L.gdr_snapshot_rollback.argtypes = [P, P, P, P, vp]
+        L.gdr_causal_conv1d.argtypes = [P, P, P, P, P, P, P, u32, vp]
         L.gdr_fwd_output_shape.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64)]
         L.gdr_ring_record_elements.argtypes = [i32, i32, i32]
         L.gdr_ring_record_elements.restype = ctypes.c_int64
         L.gdr_last_error_message.restype = ctypes.c_char_p
         L.gdr_version.restype = ctypes.c_char_p
-        for name in EXPORTS[:6]:
+        for name in EXPORTS[:7]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -191,6 +194,21 @@ def gdr_snapshot_rollback(state, state_indices, intermediate_states, accepted, *
     rc = lib().gdr_snapshot_rollback(*[_ref(d) for d in ds], _stream(stream))
     _check("gdr_snapshot_rollback", rc)
     return state
+
+
+def gdr_causal_conv1d(x, weight, input_row_offsets, *, bias=None, conv_state=None,
+                      slot_idx=None, silu=False, out=None, stream=None):
+    """Pass-1 causal depthwise Conv1d producing qkv_conv_output (page
+    "gated_delta_recurrence_fwd_gpu", Args).  Returns out (allocated here with
+    torch, x's dtype and shape, when not passed in); conv_state is updated in
+    place."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    ds = [describe(t) for t in (out, x, weight, bias, conv_state, slot_idx, input_row_offsets)]
+    rc = lib().gdr_causal_conv1d(*[_ref(d) for d in ds], GDR_FLAG_CONV_SILU if silu else 0,
+                                 _stream(stream))
+    _check("gdr_causal_conv1d", rc)
+    return out
 
 
 def gdr_fwd_output_shape(qkv_conv_output, recurrent_state):

@@ -20,7 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = [os.path.join(CSRC, "gdr_api.cpp"), os.path.join(CSRC, "gdr_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "gdr_api.cpp"), os.path.join(CSRC, "gdr_kernels.hip"),
+           os.path.join(CSRC, "gdr_conv.hip")]
 TABLE_SOURCE = os.path.join(CSRC, "gdr_rec_table.hip")
 # (work type, state storage type, kernel mode) of each recurrence table:
 # types float or uint16_t (bf16 bits); modes kPlain 0, kVerify 1, kSnap 2,

@@ -606,6 +606,80 @@ int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indic
     return hip_status(fn, gdr::launch_rollback(p, static_cast<hipStream_t>(stream)));
 }
 
+int gdr_causal_conv1d(const gdr_tensor* out, const gdr_tensor* x, const gdr_tensor* weight,
+                      const gdr_tensor* bias, const gdr_tensor* conv_state,
+                      const gdr_tensor* slot_idx, const gdr_tensor* input_row_offsets,
+                      uint32_t flags, void* stream) {
+    const char* fn = "gdr_causal_conv1d";
+    int rc;
+    if (flags & ~GDR_FLAG_CONV_SILU)
+        return fail(GDR_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, flags);
+    if ((rc = check_tensor(fn, "x", x, 2, nullptr, true, true, false))) return rc;
+    const int32_t work = x->dtype;
+    const int64_t T = x->shape[0], C = x->shape[1];
+    if (C % 4 != 0) return fail(GDR_ERR_UNSUPPORTED, "%s: channels must be a multiple of 4", fn);
+    if ((rc = check_layout(fn, "x", x, 4))) return rc;
+    if ((rc = check_tensor(fn, "out", out, 2, x->shape, true, true, false)) ||
+        (rc = check_work_dtype(fn, "out", out, work)) || (rc = check_layout(fn, "out", out, 4)))
+        return rc;
+    if (out->data == x->data) return fail(GDR_ERR_INVALID_ARG, "%s: out must not alias x", fn);
+    const int64_t wshape[2] = {C, -1};
+    if ((rc = check_tensor(fn, "weight", weight, 2, wshape, true, false, false))) return rc;
+    const int64_t W = weight->shape[1];
+    if (W < 2 || W > 4)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: kernel width %lld not built (2, 3, 4)", fn,
+                    static_cast<long long>(W));
+    if (weight->stride[1] != 1)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: weight needs unit stride over the taps", fn);
+    const int64_t cshape[1] = {C};
+    if (present(bias) && ((rc = check_tensor(fn, "bias", bias, 1, cshape, true, false, false))))
+        return rc;
+    if (present(bias) && C > 1 && bias->stride[0] != 1)
+        return fail(GDR_ERR_UNSUPPORTED, "%s: bias must be contiguous", fn);
+    if ((rc = check_tensor(fn, "input_row_offsets", input_row_offsets, 1, nullptr, false, false,
+                           true)))
+        return rc;
+    const int64_t B = input_row_offsets->shape[0] - 1;
+    if (B < 0) return fail(GDR_ERR_INVALID_ARG, "%s: input_row_offsets is empty", fn);
+    if ((rc = check_index_vec(fn, "input_row_offsets", input_row_offsets, B + 1))) return rc;
+    if (present(slot_idx) && (rc = check_index_vec(fn, "slot_idx", slot_idx, B))) return rc;
+    gdr::ConvParams p{};
+    if (present(conv_state)) {
+        const int64_t sshape[3] = {-1, W - 1, C};
+        if ((rc = check_tensor(fn, "conv_state", conv_state, 3, sshape, true, true, false)) ||
+            (rc = check_work_dtype(fn, "conv_state", conv_state, work)) ||
+            (rc = check_layout(fn, "conv_state", conv_state, 4)))
+            return rc;
+        if (!present(slot_idx) && conv_state->shape[0] < B)
+            return fail(GDR_ERR_INVALID_ARG, "%s: conv_state has fewer slots than rows", fn);
+        p.state = conv_state->data;
+        p.st_slot = conv_state->stride[0];
+        p.st_tok = conv_state->stride[1];
+    }
+    if (B == 0 || T == 0 || C == 0) {
+        g_last_error.clear();
+        return GDR_OK;
+    }
+    if (T > (int64_t{1} << 31) - 1 || B > (int64_t{1} << 20))
+        return fail(GDR_ERR_INVALID_ARG, "%s: too many tokens or rows", fn);
+    p.B = static_cast<int32_t>(B);
+    p.C = static_cast<int32_t>(C);
+    p.T = static_cast<int32_t>(T);
+    p.W = static_cast<int32_t>(W);
+    p.silu = (flags & GDR_FLAG_CONV_SILU) ? 1 : 0;
+    p.offsets = as_u32(input_row_offsets);
+    p.slot_idx = as_u32(slot_idx);
+    p.x = x->data;
+    p.x_tok = x->stride[0];
+    p.out = out->data;
+    p.o_tok = out->stride[0];
+    p.weight = static_cast<const float*>(weight->data);
+    p.w_chan = weight->stride[0];
+    p.bias = present(bias) ? static_cast<const float*>(bias->data) : nullptr;
+    return hip_status(fn, gdr::launch_conv(p, work == GDR_DTYPE_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int gdr_fwd_output_shape(const gdr_tensor* qkv_conv_output, const gdr_tensor* recurrent_state,
                          int64_t out_shape[2]) {
     const char* fn = "gdr_fwd_output_shape";

@@ -65,6 +65,19 @@ struct RollbackParams {
     int64_t block16;           // 16-byte units per (slot, head) block
 };
 
+// Pass-1 causal depthwise Conv1d over ragged rows (strides in elements).
+struct ConvParams {
+    int32_t B, C, T, W;
+    int32_t silu;
+    const uint32_t* offsets;    // [B+1]
+    const uint32_t* slot_idx;   // [B] or nullptr (slot = row); kPadSlot pads
+    const void* x; int64_t x_tok;       // [T, C], work type
+    void* out; int64_t o_tok;           // [T, C], work type
+    const float* weight; int64_t w_chan; // [C, W]
+    const float* bias;                  // [C] or nullptr
+    void* state; int64_t st_slot, st_tok;  // [slots, W-1, C], work type, or nullptr
+};
+
 enum class StateType { F32 = 0, BF16 = 1 };
 
 // Launch configuration picked by the host for one call.
@@ -82,6 +95,7 @@ hipError_t launch_recurrence(const RecParams& p, const LaunchShape& s, StateType
 hipError_t launch_fold(const FoldParams& p, const LaunchShape& s, StateType st,
                        hipStream_t stream);
 hipError_t launch_rollback(const RollbackParams& p, hipStream_t stream);
+hipError_t launch_conv(const ConvParams& p, bool work_bf16, hipStream_t stream);
 constexpr int kRollbackThreads = 256;
 constexpr int kRollbackPerThread = 8;  // 16-byte vectors per thread
 

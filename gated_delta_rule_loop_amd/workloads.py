@@ -180,6 +180,43 @@ def gdp_decode(seed: int = 1004, batch: int = 128, slots: int = 256):
                       pad_frac=0.1, state_sigma=0.05)
 
 
+def conv_inputs(rng, lengths, C, W, slots, work_dtype="f32", pad_rows=()):
+    """Inputs of the Pass-1 causal Conv1d over ragged rows: x ~ N(0, 1)
+    [T, C], weight ~ N(0, 1/W) [C, W], bias ~ N(0, 0.1) [C], history
+    conv_state ~ N(0, 1) [slots, W-1, C] (x's dtype), distinct slots."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    off = np.zeros(len(lengths) + 1, dtype=np.uint32)
+    off[1:] = np.cumsum(lengths)
+    x = rng.standard_normal((T, C)).astype(np.float32)
+    weight = (rng.standard_normal((C, W)) / np.sqrt(W)).astype(np.float32)
+    bias = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    state = rng.standard_normal((slots, W - 1, C)).astype(np.float32)
+    slot_idx = rng.choice(slots, size=len(lengths), replace=False).astype(np.uint32)
+    for r in pad_rows:
+        slot_idx[r] = PAD_SLOT_U32
+    if work_dtype == "bf16":
+        x, state = to_bf16_bits(x), to_bf16_bits(state)
+    return dict(x=x, weight=weight, bias=bias, conv_state=state, slot_idx=slot_idx,
+                row_offsets=off)
+
+
+def conv_prefill(seed: int = 1005, work_dtype="f32"):
+    """Conv1d before the ragged prefill: the prefill's row lengths (8 rows in
+    [1, 4096]), C = 2*16*128 + 32*128 = 8192 channels, W = 4, 64 slots."""
+    lengths = np.random.Generator(np.random.PCG64(1002)).integers(1, 4097, size=8)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return conv_inputs(rng, lengths, C=8192, W=4, slots=64, work_dtype=work_dtype)
+
+
+def conv_decode(seed: int = 1006, batch: int = 256, work_dtype="f32"):
+    """Conv1d before a decode step: 256 rows of one token, C = 8192, W = 4,
+    512 history slots."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return conv_inputs(rng, [1] * batch, C=8192, W=4, slots=512, work_dtype=work_dtype)
+
+
 WORKLOADS = {"tiny_ragged": tiny_ragged, "decode_step": decode_step,
              "ragged_prefill": ragged_prefill, "verify_window": verify_window,
-             "gdp_decode": gdp_decode}
+             "gdp_decode": gdp_decode, "conv_prefill": conv_prefill,
+             "conv_decode": conv_decode}

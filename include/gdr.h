@@ -59,8 +59,12 @@ extern "C" {
 /* L2 norm: x * (1 / sqrt(sum x^2 + GDR_L2NORM_EPS)). */
 #define GDR_L2NORM_EPS 1e-6f
 
-/* Head dims built: K == V in {16, 32, 64, 128}. */
-#define GDR_MAX_HEAD_DIM 128
+/* gdr_causal_conv1d flag: apply SiLU, y * sigmoid(y), to the conv output. */
+#define GDR_FLAG_CONV_SILU 2u
+
+/* Head dims built: K == V in {16, 32, 64, 128, 256}; the fused update also
+ * takes (K, V) in {(64, 128), (128, 64), (128, 256), (256, 128)}. */
+#define GDR_MAX_HEAD_DIM 256
 
 typedef struct gdr_tensor {
     void* data;
@@ -220,6 +224,37 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
 int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indices,
                           const gdr_tensor* intermediate_states, const gdr_tensor* accepted,
                           void* stream);
+
+/*
+ * gdr_causal_conv1d - the Conv1d "Pass 1" whose output is the forward's
+ * qkv_conv_output.
+ * Source: page "gated_delta_recurrence_fwd_gpu" (Args, qkv_conv_output: the
+ * conv output from Pass 1, with q, k and v at fixed channel ranges).  The page
+ * names the step only; implemented reading: a causal depthwise convolution of
+ * width W along the token axis of each ragged row, plus an optional bias,
+ * optionally followed by SiLU, where each row continues its slot's history.
+ *
+ *   out               [T, C] work dtype (f32|bf16) (out); must not alias x
+ *   x                 [T, C] work dtype: the pre-conv projections; C a
+ *                     multiple of 4, 16-byte aligned rows
+ *   weight            [C, W] f32, W in {2, 3, 4}: tap j multiplies the input
+ *                     W-1-j tokens back (unit stride over the taps)
+ *   bias              [C] f32 or absent
+ *   conv_state        [slots, W-1, C] work dtype (in/out) or absent (zero
+ *                     history, nothing written): entry i is the input W-1-i
+ *                     tokens before the row's first token; afterwards it holds
+ *                     the last W-1 inputs of history ++ row
+ *   slot_idx          [B] u32|i32 conv_state slot per row (absent: slot = row);
+ *                     0xFFFFFFFF = padding (zero output, nothing touched)
+ *   input_row_offsets [B+1] u32|i32 (B is shape[0] - 1)
+ *   flags             GDR_FLAG_CONV_SILU or 0
+ * Rows of length 0 touch nothing.  Two kernel launches on `stream` (outputs,
+ * then the history update).
+ */
+int gdr_causal_conv1d(const gdr_tensor* out, const gdr_tensor* x, const gdr_tensor* weight,
+                      const gdr_tensor* bias, const gdr_tensor* conv_state,
+                      const gdr_tensor* slot_idx, const gdr_tensor* input_row_offsets,
+                      uint32_t flags, void* stream);
 
 /*
  * gdr_fwd_output_shape - shape of recurrence_output for the given conv

@@ -159,3 +159,13 @@ def assert_state_close(got, ref, what, ref_unrounded=None, rel=REL_TOL):
 def f32_pool(state):
     """The same pool values held as float32 (to obtain unrounded oracle states)."""
     return as_f32(state).copy()
+
+
+def gpu_conv(w, *, silu=True, with_state=True):
+    """The Pass-1 Conv1d through the binding; returns (out, conv_state after)."""
+    t = {k: dev(w[k]) for k in ("x", "weight", "bias", "slot_idx", "row_offsets")}
+    st = dev(w["conv_state"]) if with_state else None
+    out = gdr.gdr_causal_conv1d(t["x"], t["weight"], t["row_offsets"], bias=t["bias"],
+                                conv_state=st, slot_idx=t["slot_idx"], silu=silu)
+    torch.cuda.synchronize()
+    return host(out), host(st)

@@ -24,9 +24,11 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gdr_recurrence_fwd", "gdr_recurrence_verify_ring", "gdr_state_fold",
-              "gdr_fused_recurrent_update", "gdr_fwd_output_shape", "gdr_ring_record_elements",
-              "gdr_last_error_message", "gdr_version"):
+              "gdr_fused_recurrent_update", "gdr_snapshot_rollback", "gdr_causal_conv1d",
+              "gdr_fwd_output_shape", "gdr_ring_record_elements", "gdr_last_error_message",
+              "gdr_version"):
         assert n in names
+    assert set(names) == set(B.EXPORTS)
 
 
 def test_library_exports_every_declared_symbol():
@@ -186,3 +188,29 @@ def test_rollback_argument_checks():
                                    None) == -1
     assert L.gdr_snapshot_rollback(r(st), r(T([0], B.GDR_DTYPE_I32)), r(inter),
                                    r(T([0], B.GDR_DTYPE_I32)), None) == 0
+
+
+def test_conv_argument_checks():
+    L = B.lib()
+    r = lambda d: None if d is None else ctypes.byref(d)  # noqa: E731
+
+    def call(**kw):
+        a = dict(out=T([10, 64], data=FAKE + 0x10000), x=T([10, 64]), w=T([64, 4]), b=None,
+                 st=T([5, 3, 64]), slot=T([3], B.GDR_DTYPE_U32), off=T([4], B.GDR_DTYPE_U32),
+                 flags=0)
+        a.update(kw)
+        return L.gdr_causal_conv1d(r(a["out"]), r(a["x"]), r(a["w"]), r(a["b"]), r(a["st"]),
+                                   r(a["slot"]), r(a["off"]), a["flags"], None)
+
+    assert call(w=T([64, 5])) == -2                               # width not built
+    assert call(w=T([64, 1])) == -2
+    assert call(x=T([10, 62]), out=T([10, 62], data=FAKE + 0x10000), w=T([62, 4]),
+                st=T([5, 3, 62])) == -2                           # channels not 4-aligned
+    assert call(out=T([10, 64], B.GDR_DTYPE_BF16, data=FAKE + 0x10000)) == -2  # work dtypes
+    assert call(st=T([5, 2, 64])) == -1                           # history must be W-1
+    assert call(st=T([5, 3, 64], B.GDR_DTYPE_BF16)) == -2         # history dtype
+    assert call(slot=T([4], B.GDR_DTYPE_U32)) == -1               # slots must be [B]
+    assert call(flags=4) == -1
+    assert call(out=T([10, 64], data=FAKE + 0x1000), x=T([10, 64], data=FAKE + 0x1000)) == -1
+    assert call(w=T([64, 4], stride=[1, 64])) == -2               # taps not unit stride
+    assert call(x=T([0, 64]), out=T([0, 64], data=FAKE + 0x10000)) == 0  # no tokens: no-op

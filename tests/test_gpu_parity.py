@@ -638,3 +638,69 @@ def test_fused_head_dims(K, V, S_draft):
     others = np.setdiff1d(np.arange(9), sl)
     assert np.array_equal(st_g[others], w["state"][others])
     say(f"K{K}V{V}: out rel err {err:.2e}, ties {ties}")
+
+
+# ------------------------------------------------------ Pass-1 causal Conv1d ---
+
+def _conv_oracle(w, silu=True, with_state=True):
+    return oracle.causal_conv1d(x=w["x"], weight=w["weight"], bias=w["bias"],
+                                conv_state=w["conv_state"] if with_state else None,
+                                slot_idx=w["slot_idx"], row_offsets=w["row_offsets"], silu=silu)
+
+
+@pytest.mark.parametrize("work", ["f32", "bf16"])
+def test_conv_prefill(work):
+    """Conv1d over the ragged prefill's rows (19,515 tokens x 8,192 channels,
+    W = 4, history, bias, SiLU) against the oracle; the new history is the
+    inputs' copy, bit for bit."""
+    w = wl.conv_prefill(work_dtype=work)
+    say(f"conv prefill {work}: T={w['x'].shape[0]} C=8192 W=4")
+    out_g, st_g = H.gpu_conv(w)
+    out_r, st_r = _conv_oracle(w)
+    if work == "bf16":
+        x32 = dict(w, x=wl.bf16_bits_to_f32(w["x"]), conv_state=wl.bf16_bits_to_f32(w["conv_state"]))
+        out_u, _ = _conv_oracle(x32)
+        ties = H.assert_state_close(out_g, out_r, "conv prefill output", out_u)
+    else:
+        ties = 0
+        H.assert_close(out_g, out_r, "conv prefill output")
+    assert np.array_equal(st_g, st_r), "conv history after the rows"
+    say(f"conv prefill {work}: ties {ties}")
+
+
+def test_conv_decode_and_continuity():
+    """Decode shape (256 rows x 1 token) against the oracle; splitting rows
+    over two calls equals one call bit for bit; zero history; padding and
+    empty rows."""
+    w = wl.conv_decode()
+    say("conv decode B=256")
+    out_g, st_g = H.gpu_conv(w)
+    out_r, st_r = _conv_oracle(w)
+    H.assert_close(out_g, out_r, "conv decode output")
+    assert np.array_equal(st_g, st_r)
+    rng = np.random.Generator(np.random.PCG64(97))
+    lengths = [9, 0, 4, 17, 1, 6]
+    v = wl.conv_inputs(rng, lengths, C=256, W=4, slots=8, pad_rows=(4,))
+    whole, st_whole = H.gpu_conv(v)
+    ref, st_ref = _conv_oracle(v)
+    H.assert_close(whole, ref, "conv ragged output")
+    assert np.array_equal(st_whole, st_ref)
+    off = v["row_offsets"].astype(np.int64)
+    cut = [3, 0, 4, 1, 1, 5]
+    st_mid = None
+    for part in (0, 1):
+        rows = [np.arange(off[b], off[b] + cut[b]) if part == 0 else
+                np.arange(off[b] + cut[b], off[b + 1]) for b in range(len(lengths))]
+        o2 = np.zeros(len(lengths) + 1, np.uint32)
+        o2[1:] = np.cumsum([len(r) for r in rows])
+        sub = dict(v, x=np.ascontiguousarray(v["x"][np.concatenate(rows)]), row_offsets=o2,
+                   conv_state=v["conv_state"] if part == 0 else st_mid)
+        out_p, st_mid = H.gpu_conv(sub)
+        assert np.array_equal(out_p.view(np.uint32), whole[np.concatenate(rows)].view(np.uint32))
+    assert np.array_equal(st_mid, st_whole)
+    z = whole[off[4]:off[5]]
+    assert not z.view(np.uint32).any()
+    assert np.array_equal(st_whole[v["slot_idx"][1]], v["conv_state"][v["slot_idx"][1]])
+    nz, _ = H.gpu_conv(v, silu=False, with_state=False)
+    nz_r, _ = _conv_oracle(v, silu=False, with_state=False)
+    H.assert_close(nz, nz_r, "conv zero-history output")
