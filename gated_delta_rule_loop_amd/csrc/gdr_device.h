@@ -7,15 +7,16 @@
 //
 // Work decomposition (ours, for 64-wide waves):
 //   * one wave owns the full K extent of BV = 8*CPL contiguous value columns of
-//     one value head: lane = 8*vl + kg holds key rows [kg*R, kg*R + R) (R = K/8)
-//     of columns [j0, j0 + CPL), j0 = 8*CPL*tile + CPL*vl.  The state stays in
-//     VGPRs for the whole row.
+//     one value head: each lane belongs to one of 8 row groups kg and holds the
+//     R = K/8 key rows [kg*R, kg*R + R) (key_row) of columns
+//     [j0, j0 + CPL), j0 = 8*CPL*tile + CPL*(column chunk).  The state stays
+//     in VGPRs for the whole row.
 //   * the K-reduction of every column (S^T k_hat and S^T q_hat) is an in-lane
-//     fused multiply-add chain over the R rows in ascending order followed by
-//     a butterfly over the 8 row groups, which are the 8 lanes of one DPP
-//     half-row (three DPP adds).  This order depends on K only, never on CPL,
-//     the chunk size or the workgroup shape, so every launch shape, the verify
-//     kernel and the fold produce identical bits.
+//     fused multiply-add chain over the lane's R rows in register order
+//     followed by a butterfly over the 8 row groups (DPP and permlane adds).
+//     This order depends on K only, never on CPL, the chunk size, the lane
+//     layout or the workgroup shape, so every launch shape, the verify kernel
+//     and the fold produce identical bits.
 //   * a workgroup is WPG waves of one (row, key head); q/k of a chunk of C
 //     tokens are normalised once per workgroup and staged in LDS together with
 //     the chunk's v, decay and beta; the next chunk's global loads are issued
@@ -158,6 +159,120 @@ __device__ __forceinline__ void store_cols(float* p, const float* s) {
     }
 }
 
+// Raw state columns, widened only where first used, so that the wait for a
+// state load can sit after the work that does not need it: bf16 pairs stay
+// packed in dwords; float values need no conversion.
+template <typename ST, int CPL>
+struct RawCols {
+    float v[CPL];
+};
+template <int CPL>
+struct RawCols<uint16_t, CPL> {
+    uint32_t v[(CPL + 1) / 2];
+};
+
+// State blocks are read once and written once per call.  Where one lane's
+// access is 16 bytes, 8 lanes cover whole 128-byte lines and the accesses are
+// non-temporal (streamed); narrower accesses leave each line to two waves,
+// which rely on the cache to merge the halves, so they stay ordinary
+// (measured: non-temporal 8-byte state accesses slowed the decode step by 20%,
+// 16-byte ones sped the snapshot-heavy fused update up by 9%).
+#ifndef GDR_NT_STATE
+#define GDR_NT_STATE 1
+#endif
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT, typename T>
+__device__ __forceinline__ T state_ld(const T* p) {
+    if constexpr (NT && GDR_NT_STATE) return __builtin_nontemporal_load(p);
+    return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void state_st(T v, T* p) {
+    if constexpr (NT && GDR_NT_STATE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <int CPL>
+__device__ __forceinline__ void load_raw_cols(const float* p, RawCols<float, CPL>& r) {
+    if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; i += 4) {
+            const f32x4_t w = state_ld<true>(reinterpret_cast<const f32x4_t*>(p + i));
+            r.v[i] = w.x; r.v[i + 1] = w.y; r.v[i + 2] = w.z; r.v[i + 3] = w.w;
+        }
+    } else if constexpr (CPL == 2) {
+        const f32x2_t w = state_ld<false>(reinterpret_cast<const f32x2_t*>(p));
+        r.v[0] = w.x; r.v[1] = w.y;
+    } else {
+        r.v[0] = state_ld<false>(p);
+    }
+}
+template <int CPL>
+__device__ __forceinline__ void load_raw_cols(const uint16_t* p, RawCols<uint16_t, CPL>& r) {
+    if constexpr (CPL == 8) {
+        const u32x4_t w = state_ld<true>(reinterpret_cast<const u32x4_t*>(p));
+        r.v[0] = w.x; r.v[1] = w.y; r.v[2] = w.z; r.v[3] = w.w;
+    } else if constexpr (CPL == 4) {
+        const u32x2_t w = state_ld<false>(reinterpret_cast<const u32x2_t*>(p));
+        r.v[0] = w.x; r.v[1] = w.y;
+    } else if constexpr (CPL == 2) {
+        r.v[0] = state_ld<false>(reinterpret_cast<const uint32_t*>(p));
+    } else {
+        r.v[0] = state_ld<false>(p);
+    }
+}
+
+// A state row fragment: CPL values stored (bf16 rounded to nearest even).
+template <int CPL>
+__device__ __forceinline__ void store_state_cols(float* p, const float* s) {
+    if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; i += 4)
+            state_st<true>(f32x4_t{s[i], s[i + 1], s[i + 2], s[i + 3]},
+                     reinterpret_cast<f32x4_t*>(p + i));
+    } else if constexpr (CPL == 2) {
+        state_st<false>(f32x2_t{s[0], s[1]}, reinterpret_cast<f32x2_t*>(p));
+    } else {
+        state_st<false>(s[0], p);
+    }
+}
+template <int CPL>
+__device__ __forceinline__ void store_state_cols(uint16_t* p, const float* s) {
+    if constexpr (CPL == 8) {
+        state_st<true>(u32x4_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
+                         pack_bf16x2(s[6], s[7])},
+                 reinterpret_cast<u32x4_t*>(p));
+    } else if constexpr (CPL == 4) {
+        state_st<false>(u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])},
+                 reinterpret_cast<u32x2_t*>(p));
+    } else if constexpr (CPL == 2) {
+        state_st<false>(pack_bf16x2(s[0], s[1]), reinterpret_cast<uint32_t*>(p));
+    } else {
+        store_cols<1>(p, s);
+    }
+}
+template <int CPL>
+__device__ __forceinline__ void widen_cols(const RawCols<float, CPL>& r, float* o) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[c] = r.v[c];
+}
+template <int CPL>
+__device__ __forceinline__ void widen_cols(const RawCols<uint16_t, CPL>& r, float* o) {
+    if constexpr (CPL == 1) {
+        o[0] = __uint_as_float(r.v[0] << 16);
+    } else {
+#pragma unroll
+        for (int j = 0; j < CPL / 2; ++j) {
+            o[2 * j] = bf16_lo(r.v[j]);
+            o[2 * j + 1] = bf16_hi(r.v[j]);
+        }
+    }
+}
+
 // ---------------------------------------------------- per-lane arithmetic ---
 
 // The state of one (row, value head) is held as scale * S: a token's decay
@@ -192,8 +307,18 @@ __device__ __forceinline__ void dot_rows(const float (&S)[R][CPL], const float (
     }
 }
 
-// The R rows [kg*R, kg*R + R) of a K-vector staged in LDS with 4 floats of
-// padding after every R (so the 8 row groups hit different banks).
+// Key rows of a lane: row group kg (of 8) holds the R = K/8 consecutive key
+// rows kg*R + ri.  Every kernel (forward, verify, fold) uses this one mapping,
+// so their reduction orders stay identical.  (Interleaving the groups, row
+// ri*8 + kg, was measured slower for the decode step and the fold.)
+template <int R>
+__device__ __forceinline__ int key_row(int kg, int ri) { return kg * R + ri; }
+
+// A staged K-vector in LDS: row group kg's R values at kg*(R + 4), 4 floats
+// of padding after each group so the 8 groups hit different banks.
+template <int R>
+__device__ __forceinline__ int stage_pos(int idx) { return idx + (idx / R) * 4; }
+
 template <int R>
 __device__ __forceinline__ void read_rows(const float* vec, int kg, float (&out)[R]) {
     const float* src = vec + kg * (R + 4);
@@ -209,10 +334,10 @@ __device__ __forceinline__ void read_rows(const float* vec, int kg, float (&out)
     }
 }
 
-template <int R>
-__device__ __forceinline__ int pad_index(int i) { return i + (i / R) * 4; }
-
 // ------------------------------------------------------------- recurrence ---
+
+// Zeros read in place of the state rows when there is no source state.
+__device__ __attribute__((aligned(16))) float kZeroRow[16];
 
 // Kernel modes: kPlain, kVerify or kSnap, plus the kBetaCols bit when beta
 // carries one value per value column.
@@ -340,18 +465,26 @@ struct Rec {
         for (int t = 0; t < it.L; ++t) store_cols<CPL>(outp + t * p.o_tok, z);
     }
 
-    __device__ static void load_state(const RecParams& p, const Item& it, int kg,
-                                      float (&S)[R][CPL]) {
-        if (p.src) {
-            const ST* sp = src_ptr(p, it);
+    // The lane's state rows as loaded (see RawCols).
+    struct RawState {
+        RawCols<ST, CPL> row[R];
+    };
+
+    // Without a source state every row is read from kZeroRow (row stride 0),
+    // so the loads are unconditional and one wait covers them on every path.
+    __device__ static void load_state(const RecParams& p, const Item& it, int kg, RawState& rs) {
+        static_assert(CPL * sizeof(ST) <= sizeof(kZeroRow), "zero row");
+        const bool has = p.src != nullptr;
+        const ST* sp = has ? src_ptr(p, it) : reinterpret_cast<const ST*>(kZeroRow);
+        const int row_stride = has ? V : 0;
 #pragma unroll
-            for (int ri = 0; ri < R; ++ri) load_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
-        } else {
+        for (int ri = 0; ri < R; ++ri)
+            load_raw_cols<CPL>(sp + key_row<R>(kg, ri) * row_stride, rs.row[ri]);
+    }
+
+    __device__ static void widen_state(const RawState& rs, float (&S)[R][CPL]) {
 #pragma unroll
-            for (int ri = 0; ri < R; ++ri)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) S[ri][c] = 0.0f;
-        }
+        for (int ri = 0; ri < R; ++ri) widen_cols<CPL>(rs.row[ri], S[ri]);
     }
 
     // Stores the state scale * S.
@@ -361,7 +494,7 @@ struct Rec {
             float row[CPL];
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) row[cc] = scale * S[ri][cc];
-            store_cols<CPL>(base + (kg * R + ri) * V, row);
+            store_state_cols<CPL>(base + key_row<R>(kg, ri) * V, row);
         }
     }
 
@@ -483,8 +616,8 @@ struct Rec {
                 const int idx = lane + 64 * e;
                 if (idx < K) {
                     const float kh = kv[e] * rk;
-                    B[OFF_K + tau * KP + pad_index<R>(idx)] = kh;
-                    B[OFF_Q + tau * KP + pad_index<R>(idx)] = qv[e] * rqs;
+                    B[OFF_K + tau * KP + stage_pos<R>(idx)] = kh;
+                    B[OFF_Q + tau * KP + stage_pos<R>(idx)] = qv[e] * rqs;
                     if (rec_k) ring_put(p, rec + (tc + tau) * p.ring_tok + idx, kh);
                 }
             }
@@ -610,15 +743,21 @@ struct Rec {
             p, it, c, B, S, scale, w, lane);
     }
 
-    // All chunks of an item whose state is scale * S and whose chunk-0 inputs
-    // are in st.
+    // All chunks of an item whose loaded state is rs and whose chunk-0 inputs
+    // are in st; leaves the final state as scale * S.  The state is widened
+    // after the first stage is committed, so its loads complete under that
+    // work.
     template <int MODE>
-    __device__ static void run_item(const RecParams& p, const Item& it, float (&S)[R][CPL],
-                                    float& scale, Stage& st, float* lds, int w, int lane) {
+    __device__ static void run_item(const RecParams& p, const Item& it, const RawState& rs,
+                                    float (&S)[R][CPL], float& scale, Stage& st, float* lds,
+                                    int w, int lane) {
         constexpr bool BC = (MODE & kBetaCols) != 0;
         constexpr int BUF = buf<BC>();
         commit_stage<BC>(p, it, 0, st, lds, w, lane);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);  // keep the widening (and its wait) here
+        widen_state(rs, S);
+        scale = 1.0f;
         const int nch = (it.L + C - 1) / C;
         for (int c = 0; c < nch; ++c) {
             const bool next = c + 1 < nch;
@@ -654,10 +793,11 @@ __global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecPa
     // are in flight together.
     typename Q::Stage st;
     Q::template load_stage<(MODE & kBetaCols) != 0>(p, it, 0, st, w, lane);
+    typename Q::RawState rs;
+    Q::load_state(p, it, kg, rs);
     float S[Q::R][CPL];
-    Q::load_state(p, it, kg, S);
-    float scale = 1.0f;
-    Q::template run_item<MODE>(p, it, S, scale, st, lds, w, lane);
+    float scale;
+    Q::template run_item<MODE>(p, it, rs, S, scale, st, lds, w, lane);
     Q::store_state(p, it, kg, scale, S);
 }
 

@@ -102,7 +102,11 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
              static_cast<int64_t>(hv) * p.st_head + j0;
     float S[R][CPL];
 #pragma unroll
-    for (int ri = 0; ri < R; ++ri) load_cols<CPL>(sp + (kg * R + ri) * V, S[ri]);
+    for (int ri = 0; ri < R; ++ri) {
+        RawCols<ST, CPL> raw;
+        load_raw_cols<CPL>(sp + key_row<R>(kg, ri) * V, raw);
+        widen_cols<CPL>(raw, S[ri]);
+    }
 
     const RT* rec = static_cast<const RT*>(p.ring) +
                     static_cast<int64_t>(p.ring_idx[row]) * p.ring_row +
@@ -113,7 +117,7 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
         float a;
         load_cols<1>(r + K + p.G * V + m, &a);
         float kr[R];
-        load_run<R>(r + kg * R, kr);
+        load_run<R>(r + key_row<R>(kg, 0), kr);
         float u[CPL];
         load_cols<CPL>(r + K + m * V + j0, u);
         scale = decay_step<R, CPL>(S, scale * a);
@@ -130,7 +134,7 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
         float row[CPL];
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) row[cc] = scale * S[ri][cc];
-        store_cols<CPL>(sp + (kg * R + ri) * V, row);
+        store_state_cols<CPL>(sp + key_row<R>(kg, ri) * V, row);
     }
 }
 
@@ -161,11 +165,11 @@ __global__ void __launch_bounds__(kRollbackThreads) rollback_kernel(const Rollba
         // whole chunk in range: all loads in flight before the first store
         u32x4 v[kRollbackPerThread];
 #pragma unroll
-        for (int j = 0; j < kRollbackPerThread; ++j) v[j] = src[base + j * kRollbackThreads];
+        for (int j = 0; j < kRollbackPerThread; ++j) v[j] = state_ld<true>(src + base + j * kRollbackThreads);
 #pragma unroll
-        for (int j = 0; j < kRollbackPerThread; ++j) dst[base + j * kRollbackThreads] = v[j];
+        for (int j = 0; j < kRollbackPerThread; ++j) state_st<true>(v[j], dst + base + j * kRollbackThreads);
     } else {
-        for (int64_t i = base; i < p.block16; i += kRollbackThreads) dst[i] = src[i];
+        for (int64_t i = base; i < p.block16; i += kRollbackThreads) state_st<true>(state_ld<true>(src + i), dst + i);
     }
 }
 }  // namespace
