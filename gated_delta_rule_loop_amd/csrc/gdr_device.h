@@ -773,11 +773,11 @@ struct Rec {
 
 // One work item per workgroup.
 // One-token stages are the HBM-bound decode shape: ask for 4 waves per SIMD.
-template <int C>
-constexpr int kMinWaves = C == 1 ? 4 : 1;
+template <int C, int CPL>
+constexpr int kMinWaves = C == 1 ? (CPL <= 4 ? 4 : 2) : 1;
 
 template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
-__global__ void __launch_bounds__(WPG * 64, kMinWaves<C>) rec_kernel(const RecParams p) {
+__global__ void __launch_bounds__(WPG * 64, (kMinWaves<C, CPL>)) rec_kernel(const RecParams p) {
     using Q = Rec<K, V, CPL, C, WPG, ST, KG_LOW, WT>;
     __shared__ __attribute__((aligned(16))) float lds[2 * Q::template buf<(MODE & kBetaCols) != 0>()];
     const int lane = threadIdx.x & 63;

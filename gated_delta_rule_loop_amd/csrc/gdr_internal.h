@@ -104,7 +104,7 @@ constexpr int kRollbackPerThread = 8;  // 16-byte vectors per thread
 // decode (about one token per row), short windows (verify), the fused update
 // on short rows (GDP decode, snapshot-heavy), and long rows (prefill).
 #ifndef GDR_DECODE_CPL
-#define GDR_DECODE_CPL 4
+#define GDR_DECODE_CPL 8
 #endif
 #ifndef GDR_DECODE_CHUNK
 #define GDR_DECODE_CHUNK 1
