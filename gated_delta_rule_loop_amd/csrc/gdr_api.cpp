@@ -145,7 +145,11 @@ gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t to
     s.V = static_cast<int>(V);
     const bool long_rows = rows > 0 && total_tokens >= 16 * rows;
     const bool decode = rows > 0 && 2 * total_tokens <= 3 * rows;  // ~1 token per row
-    if (K == 256 || K != V) {  // one short and one long-row shape per pair
+    if (K == 128 && K != V && e == Entry::Fused && !long_rows) {
+        s.cpl = GDR_FUSED_CPL;  // as the K == V == 128 fused profile
+        s.chunk = GDR_FUSED_CHUNK;
+        s.kg_low = GDR_FUSED_KGLOW;
+    } else if (K == 256 || K != V) {  // one short and one long-row shape per pair
         if (e == Entry::Fold || !long_rows) {
             s.cpl = K == 256 ? 2 : (K == 64 ? 8 : 4);
             s.chunk = e == Entry::Fold ? 1 : 8;

@@ -848,6 +848,8 @@ hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_
         GDR_REC_CASE(128, 64, 4, 8, false)
         GDR_REC_CASE(128, 64, 1, 16, true)
         GDR_REC_CASE(128, 256, 4, 8, false)
+        GDR_REC_CASE(128, 256, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
+        GDR_REC_CASE(128, 64, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
         GDR_REC_CASE(128, 256, 1, 16, true)
         GDR_REC_CASE(256, 128, 2, 8, false)
         GDR_REC_CASE(256, 128, 1, 8, true)
