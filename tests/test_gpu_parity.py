@@ -704,3 +704,57 @@ def test_conv_decode_and_continuity():
     nz, _ = H.gpu_conv(v, silu=False, with_state=False)
     nz_r, _ = _conv_oracle(v, silu=False, with_state=False)
     H.assert_close(nz, nz_r, "conv zero-history output")
+
+
+# ------------------------------------------------------------- degenerate ---
+
+@pytest.mark.parametrize("lengths", [[200, 37, 300, 5, 64, 1], [8, 3, 1, 6, 7, 2]])
+def test_extreme_decays(lengths):
+    """Decays that drive the scaled state through its renormalisation: tiny
+    (1e-3 and 1e-30 per token, far past 2^-64 in a few tokens), exact zeros
+    mid-row, exactly 1, slightly above 1, and mixed; beta = 0 on some tokens.
+    Long-row and short-row shapes against the oracle; verify == forward and
+    fold(n) == forward(prefix n) bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(401))
+    w = wl.packed_inputs(rng, lengths, nk=2, nv=4, K=128, V=128, slots=8, state_dtype="f32",
+                         state_sigma=0.3)
+    off = w["row_offsets"].astype(np.int64)
+    patterns = [1e-3, 1e-30, 1.0, 1.01, None, 0.5]
+    for b, pat in enumerate(patterns[:len(lengths)]):
+        seg = slice(off[b], off[b + 1])
+        if pat is None:  # zeros at every 7th token, random elsewhere
+            d = w["decay"][seg]
+            d[::7] = 0.0
+        else:
+            w["decay"][seg] = pat
+    w["beta"][::5] = 0.0
+    say(f"extreme decays, lengths {lengths}")
+    out_g, st_g = check_fwd_against_oracle(w, f"extreme decays {lengths}")
+    assert np.isfinite(out_g).all() and np.isfinite(st_g).all()
+    ring_len = 8
+    G, K, V = 2, 128, 128
+    w["ring"] = np.zeros((8, 2, ring_len, wl.ring_record_stride(G, K, V)), np.float32)
+    w["ring_slot_idx"] = np.arange(len(lengths), dtype=np.uint32)
+    out_v, st_v, ring_v = H.gpu_verify(w)
+    assert np.array_equal(out_v.view(np.uint32), out_g.view(np.uint32))
+    lens = np.diff(off)
+    acc = np.array([max(1, L // 2) if L <= ring_len else L for L in lens], np.uint32)
+    folded = H.gpu_fold(w, st_v, ring_v, acc)
+    keep = np.concatenate([np.arange(off[b], off[b] + acc[b]) for b in range(len(lens))])
+    offs = np.zeros(len(lens) + 1, np.uint32)
+    offs[1:] = np.cumsum(acc)
+    _, st_pre = H.gpu_fwd(dict(w, qkv=w["qkv"][keep], decay=w["decay"][keep],
+                               beta=w["beta"][keep], row_offsets=offs))
+    for b in range(len(lens)):
+        s = w["slot_idx"][b]
+        assert np.array_equal(folded[s].view(np.uint32), st_pre[s].view(np.uint32)), b
+
+
+def test_large_decode_batch():
+    """2048 one-token rows (8,192 workgroups) against the oracle: index
+    arithmetic of large grids, every row checked."""
+    rng = np.random.Generator(np.random.PCG64(402))
+    w = wl.packed_inputs(rng, [1] * 2048, nk=4, nv=8, K=128, V=128, slots=4096,
+                         state_dtype="bf16", state_sigma=0.05)
+    say("large decode batch: 2048 rows x 8 value heads")
+    check_fwd_against_oracle(w, "large decode batch")
