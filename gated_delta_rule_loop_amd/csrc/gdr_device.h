@@ -73,6 +73,64 @@ __device__ __forceinline__ float sum_row_groups(float x) {
     return x;
 }
 
+// Several columns at once in the row-groups-high layout, same pairs and
+// association as sum_row_groups<false> (so the same bits): after the DPP step
+// each permlane swap carries two columns - a swap of (a, b) followed by one add
+// leaves a's pair sums in some 16-lane rows and b's in the others.
+__device__ __forceinline__ float pair16_sum(float a, float b) {
+    // rows 0 and 2 get a[r] + a[r+1], rows 1 and 3 get b[r-1] + b[r]
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float a, float b) {
+    // lanes 0-31 get a[lane] + a[lane + 32], lanes 32-63 get b[lane - 32] + b[lane]
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                              false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Column totals of CPL (2, 4 or 8) columns, spread over the 16-lane rows r:
+// CPL 2: y[0] = column r & 1; CPL 4: y[0] = column r; CPL 8: y[0] = column r,
+// y[1] = column 4 + r.
+template <int CPL>
+constexpr int kSpread = CPL == 8 ? 2 : 1;
+template <int CPL>
+__device__ __forceinline__ void sum_cols_spread(float (&x)[CPL], float (&y)[kSpread<CPL>]) {
+    static_assert(CPL == 2 || CPL == 4 || CPL == 8, "spread reduction");
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) x[c] = x[c] + dpp<0x128>(x[c]);  // lane ^ 8
+    if constexpr (CPL == 2) {
+        y[0] = xor32_sum(pair16_sum(x[0], x[1]));
+    } else {
+        y[0] = pair32_sum(pair16_sum(x[0], x[1]), pair16_sum(x[2], x[3]));
+        if constexpr (CPL == 8)
+            y[1] = pair32_sum(pair16_sum(x[4], x[5]), pair16_sum(x[6], x[7]));
+    }
+}
+
+// Back from the spread form: every lane gets all CPL column totals.
+template <int CPL>
+__device__ __forceinline__ void spread_to_all(const float (&y)[kSpread<CPL>], float (&x)[CPL]) {
+    auto both16 = [](float v, float& lo, float& hi) {  // rows [a b a b] -> [a..], [b..]
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+        lo = __uint_as_float(r[0]);
+        hi = __uint_as_float(r[1]);
+    };
+    if constexpr (CPL == 2) {
+        both16(y[0], x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kSpread<CPL>; ++i) {  // rows [a b c d] -> [a b a b], [c d c d]
+            auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[i]),
+                                                      __float_as_uint(y[i]), false, false);
+            both16(__uint_as_float(r[0]), x[4 * i + 0], x[4 * i + 1]);
+            both16(__uint_as_float(r[1]), x[4 * i + 2], x[4 * i + 3]);
+        }
+    }
+}
+
 // Sum over the whole wave, identical in every lane.
 __device__ __forceinline__ float sum_wave(float x) {
     x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
@@ -635,6 +693,23 @@ struct Rec {
         }
     }
 
+    // Column totals of a lane's CPL columns in every lane: through the spread
+    // form in the row-groups-high layout (two columns per permlane swap),
+    // column by column otherwise.  Both give the bits of sum_row_groups.
+    // (Multi-token stages only: the one-token decode stage is bound by HBM and
+    // measured a little faster column by column.)
+    static constexpr bool kSpreadOut = !KG_LOW && C > 1 && (CPL == 2 || CPL == 4 || CPL == 8);
+    __device__ static void sum_cols_all(float (&x)[CPL]) {
+        if constexpr (kSpreadOut) {
+            float y[kSpread<CPL>];
+            sum_cols_spread<CPL>(x, y);
+            spread_to_all<CPL>(y, x);
+        } else {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
+        }
+    }
+
     // The tokens of chunk c, staged in B.  The state before the chunk is
     // scale * S; both are updated (see decay_step for the representation).
     // REC: record the ring for rows that fit it (verify); SNAP: store snapshots.
@@ -665,8 +740,7 @@ struct Rec {
         read_rows<R>(B + OFF_K, kg, kr);
         float x[CPL];  // S^T k_hat of the current token, before the scale
         dot_rows<R, CPL>(S, kr, x);
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
+        sum_cols_all(x);
 
         for (int tau = 0; tau < Lc; ++tau) {
             const float a = B[OFF_A + w * C + tau];
@@ -702,13 +776,27 @@ struct Rec {
             if (C > 1 && tau + 1 < Lc) {
                 read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
                 dot_rows<R, CPL>(S, kr, x);
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<KG_LOW>(x[cc]);
+                sum_cols_all(x);
             }
+            if constexpr (kSpreadOut) {
+                // totals spread over the rows: lanes of even row groups store
+                // their row's column(s)
+                float y[kSpread<CPL>];
+                sum_cols_spread<CPL>(o, y);
+                const int r = lane >> 4;
+                if ((lane & 8) == 0 && (CPL != 2 || lane < 32)) {
+                    const int col = CPL == 2 ? (r & 1) : r;
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups<KG_LOW>(o[cc]);
-
-            if (kg == 0) store_cols<CPL>(outp, o);
+                    for (int i = 0; i < kSpread<CPL>; ++i) {
+                        const float val = scale * y[i];
+                        store_cols<1>(outp + col + 4 * i, &val);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups<KG_LOW>(o[cc]);
+                if (kg == 0) store_cols<CPL>(outp, o);
+            }
             outp += p.o_tok;
             if (REC && it.record) {
                 const int64_t ru = rec + K + it.m * V + it.j0;
