@@ -138,6 +138,19 @@ float resolve_scale(float scale, int64_t K) {
 // not depend on this choice.
 enum class Entry { Packed, Fused, Fold };
 
+// Longest rows first for ragged short-row batches (multi-token stages, row
+// groups in the high lane bits: the verify and short-window shapes) small
+// enough for every workgroup to rank the rows itself, when the grid is larger
+// than what one pass of the chip holds at once (256 compute units, about 4
+// workgroups each): a grid that is resident as a whole gains nothing from the
+// order.  The long-row shapes run without it (their code is compiled without
+// the ranking).
+int32_t order_rows(const gdr::LaunchShape& s, const gdr::RecParams& p) {
+    const int64_t grid = int64_t{p.rows} * p.nk * p.parts;
+    return p.offsets != nullptr && p.rows >= 2 && p.rows <= gdr::kOrderMaxRows &&
+           s.chunk > 1 && !s.kg_low && grid > 4 * 256;
+}
+
 gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t total_tokens,
                             int64_t rows) {
     gdr::LaunchShape s{};
@@ -316,6 +329,7 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     p.spt = 1;
     p.scale = resolve_scale(scale, K);
     p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
+    p.order = order_rows(s, p);
     const gdr::StateType st =
         state->dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
     return hip_status(fn, gdr::launch_recurrence(p, s, st, work == GDR_DTYPE_BF16,
@@ -560,6 +574,7 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     p.spt = steps_per_token;
     p.scale = resolve_scale(scale, K);
     p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
+    p.order = order_rows(s, p);
     const gdr::StateType st =
         st_dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
     return hip_status(fn, gdr::launch_recurrence(p, s, st, work == GDR_DTYPE_BF16,

@@ -344,7 +344,7 @@ constexpr float kScaleHi = 1.8446744073709552e19f;  // 2^64
 
 template <int R, int CPL>
 __device__ __forceinline__ float decay_step(float (&S)[R][CPL], float cn) {
-    if (cn >= kScaleLo && cn <= kScaleHi) return cn;
+    if (__builtin_expect(cn >= kScaleLo && cn <= kScaleHi, 1)) return cn;
 #pragma unroll
     for (int ri = 0; ri < R; ++ri)
 #pragma unroll
@@ -719,7 +719,9 @@ struct Rec {
         const int kg = row_group(lane);
         const int vc = col_chunk(lane) * CPL;
         const int tc = c * C;
-        const int Lc = min(C, it.L - tc);
+        // Tokens of this chunk; made a scalar for the multi-token loops (the
+        // one-token decode stage measured a little faster without)
+        const int Lc = C > 1 ? __builtin_amdgcn_readfirstlane(min(C, it.L - tc)) : min(C, it.L - tc);
         WT* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
         int64_t rec = 0;  // ring element offset of this token's record
         if (REC && it.record)
@@ -795,7 +797,11 @@ struct Rec {
             } else {
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) o[cc] = scale * sum_row_groups<KG_LOW>(o[cc]);
-                if (kg == 0) store_cols<CPL>(outp, o);
+                // Every lane holds its columns' totals.  With the row groups in
+                // the low lane bits the 8 lanes of a column store the same bits
+                // to the same address, which spares the long-row loop a lane
+                // mask and its branches.
+                if (KG_LOW || kg == 0) store_cols<CPL>(outp, o);
             }
             outp += p.o_tok;
             if (REC && it.record) {
@@ -859,6 +865,60 @@ struct Rec {
     }
 };
 
+// Row of the given rank when rows are taken longest first (ties by index):
+// long rows start early and short ones fill the end of the launch, instead of
+// a long row that happens to sit late in the batch starting last.  Every
+// workgroup ranks the rows itself from the offsets: each row's length bucket
+// and a bucket histogram in LDS, a wave prefix sum over the histogram, then a
+// ballot scan for the k-th row of the rank's bucket.  Called by every thread
+// of the workgroup (two barriers) with kOrderBuckets + B words of LDS;
+// returns a wave-uniform row in [0, B).
+__device__ inline uint32_t order_bucket(uint32_t len) {
+    const uint32_t top = kOrderBuckets - 1;
+    return top - (len < top ? len : top);  // bucket 0 holds the longest rows
+}
+
+__device__ int ordered_row(const uint32_t* off, int B, int rank, uint32_t* scratch) {
+    static_assert(kOrderBuckets == 64, "one bucket per lane");
+    uint32_t* hist = scratch;
+    uint32_t* bucket_of = scratch + kOrderBuckets;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    if (t < kOrderBuckets) hist[t] = 0;
+    __syncthreads();
+    for (int i = t; i < B; i += blockDim.x) {
+        const uint32_t b = order_bucket(off[i + 1] - off[i]);
+        bucket_of[i] = b;
+        atomicAdd(&hist[b], 1u);
+    }
+    __syncthreads();
+    const uint32_t h = hist[lane];
+    uint32_t incl = h;  // inclusive prefix sum over the 64 buckets
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t x = __shfl_up(incl, d);
+        if (lane >= d) incl += x;
+    }
+    const uint32_t r = static_cast<uint32_t>(rank);
+    const uint64_t hit = __ballot(incl - h <= r && r < incl);
+    if (hit == 0) return rank;  // rank >= B: not reached for a valid launch
+    const int bucket = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    int k = static_cast<int>(r - __shfl(incl - h, bucket));
+    for (int c = 0; c < B; c += 64) {
+        const int i = c + lane;
+        const bool m = i < B && static_cast<int>(bucket_of[i]) == bucket;
+        const uint64_t mask = __ballot(m);
+        const int cnt = __popcll(mask);
+        if (k < cnt) {
+            const int below = __popcll(mask & ((uint64_t{1} << lane) - 1));
+            const uint64_t sel = __ballot(m && below == k);
+            return c + __ffsll(static_cast<unsigned long long>(sel)) - 1;
+        }
+        k -= cnt;
+    }
+    return rank;
+}
+
 // One work item per workgroup.
 // One-token stages are the HBM-bound decode shape: ask for 4 waves per SIMD.
 template <int C, int CPL>
@@ -871,7 +931,20 @@ __global__ void __launch_bounds__(WPG * 64, (kMinWaves<C, CPL>)) rec_kernel(cons
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int kg = Q::row_group(lane);
-    const Item it = Q::item(p, blockIdx.x, w, lane);
+    int idx = blockIdx.x;
+    if (C > 1 && !KG_LOW && p.order) {  // set for the multi-token row-groups-high shapes only
+        const int per_row = p.parts * p.nk;
+        const int rank = idx / per_row;
+        // The ranking's LDS is the second stage buffer: the first write there
+        // (chunk 1's commit) comes after a barrier that every wave reaches
+        // only once it has ranked.
+        constexpr int BUF = Q::template buf<(MODE & kBetaCols) != 0>();
+        static_assert(C == 1 || KG_LOW || BUF >= kOrderBuckets + kOrderMaxRows, "ranking LDS");
+        uint32_t* scratch = reinterpret_cast<uint32_t*>(lds + BUF);
+        const int row = __builtin_amdgcn_readfirstlane(ordered_row(p.offsets, p.rows, rank, scratch));
+        idx = row * per_row + (idx - rank * per_row);
+    }
+    const Item it = Q::item(p, idx, w, lane);
     if (it.pad) {
         Q::zero_output(p, it, lane);
         return;

@@ -44,7 +44,14 @@ struct RecParams {
 
     float scale;
     int32_t l2norm;
+    int32_t order;   // 1: workgroups take the rows longest first (offsets, <= kOrderMaxRows rows)
 };
+
+// Longest-first row order: lengths are bucketed (kOrderBuckets buckets, the
+// last one holding every length >= kOrderBuckets - 1), and every workgroup
+// ranks the rows itself, so it is offered for small batches only.
+constexpr int kOrderBuckets = 64;
+constexpr int kOrderMaxRows = 256;
 
 struct FoldParams {
     int32_t rows, nv, nk, G, parts;

@@ -758,3 +758,20 @@ def test_large_decode_batch():
                          state_dtype="bf16", state_sigma=0.05)
     say("large decode batch: 2048 rows x 8 value heads")
     check_fwd_against_oracle(w, "large decode batch")
+
+
+@pytest.mark.parametrize("rows", [256, 257])
+def test_longest_first_row_order(rows):
+    """Ragged batches at the row-ordering limit (256 rows, 2,048 workgroups:
+    workgroups take rows longest first) and one past it (index order):
+    lengths with many ties,
+    empty rows, lengths past the last length bucket and a padding row; every
+    row against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(403))
+    lengths = rng.choice([0, 1, 2, 3, 5, 8, 12, 13, 20, 62, 63, 64, 75], size=rows,
+                         p=[.05, .2, .15, .1, .1, .1, .1, .05, .05, .03, .03, .02, .02])
+    w = P.small_packed(404, lengths, nk=4, nv=8, K=128, V=128, slots=rows + 11,
+                       state_dtype="bf16", sigma=0.05)
+    w["slot_idx"][rows // 3] = wl.PAD_SLOT_U32
+    say(f"row order: {rows} rows, {int(lengths.sum())} tokens")
+    check_fwd_against_oracle(w, f"row order {rows}")
