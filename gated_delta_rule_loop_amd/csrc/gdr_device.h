@@ -339,12 +339,18 @@ __device__ __forceinline__ void widen_cols(const RawCols<uint16_t, CPL>& r, floa
 // [2^-64, 2^64] (a zero decay included) the scale is folded into the registers
 // and reset to 1.  The forward, the verify and the fold run this same scalar
 // sequence from the same decays, so their states stay bit-identical.
-constexpr float kScaleLo = 5.421010862427522e-20f;  // 2^-64
-constexpr float kScaleHi = 1.8446744073709552e19f;  // 2^64
+constexpr uint32_t kScaleLoBits = 0x1F800000u;  // 2^-64
+constexpr uint32_t kScaleHiBits = 0x5F800000u;  // 2^64
+
+// cn in [2^-64, 2^64], by one unsigned compare: positive floats order as their
+// bit patterns, and zero, negative values and NaN all fall outside.
+__device__ __forceinline__ bool scale_in_range(float cn) {
+    return __float_as_uint(cn) - kScaleLoBits <= kScaleHiBits - kScaleLoBits;
+}
 
 template <int R, int CPL>
 __device__ __forceinline__ float decay_step(float (&S)[R][CPL], float cn) {
-    if (__builtin_expect(cn >= kScaleLo && cn <= kScaleHi, 1)) return cn;
+    if (__builtin_expect(scale_in_range(cn), 1)) return cn;
 #pragma unroll
     for (int ri = 0; ri < R; ++ri)
 #pragma unroll
