@@ -938,6 +938,14 @@ __global__ void __launch_bounds__(WPG * 64, (kMinWaves<C, CPL>)) rec_kernel(cons
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int kg = Q::row_group(lane);
     int idx = blockIdx.x;
+    // Workgroups are dispatched to the 8 XCDs round robin (block b to XCD
+    // b % 8).  The parts of one (row, key head) read the same q and k, so they
+    // are given blocks 8 apart: one XCD, one L2, while consecutive (row, key
+    // head) pairs still spread over all XCDs.
+    if (p.parts > 1 && (p.rows * p.nk) % 8 == 0) {
+        const int q = idx >> 3;
+        idx = ((q / p.parts) * 8 + (idx & 7)) * p.parts + q % p.parts;
+    }
     if (C > 1 && !KG_LOW && p.order) {  // set for the multi-token row-groups-high shapes only
         const int per_row = p.parts * p.nk;
         const int rank = idx / per_row;
