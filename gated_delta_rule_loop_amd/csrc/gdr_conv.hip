@@ -13,10 +13,13 @@
 // wave reads 1 KiB of one token row) and a run of CH consecutive tokens, whose
 // inputs it loads up front; it slides a window of the W-1 previous inputs in
 // registers and refills it from the history or from x when it crosses into a
-// new row.  conv_state_kernel then writes each row's new history; running it
-// after the first launch is what keeps the in-place history update free of
-// races (every output that reads the old history has been computed).  The work
-// is a stream over x, out and the history: HBM-bound, no LDS.
+// new row.  conv_state_kernel then writes the new history of rows of two or
+// more tokens; running it after the first launch is what keeps the in-place
+// history update free of races (every output that reads the old history has
+// been computed).  A one-token row (a decode step) has a single reader of its
+// history, the thread of its token, which writes the new history itself, so a
+// decode step reads the history once.  The work is a stream over x, out and
+// the history: HBM-bound, no LDS.
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -128,11 +131,20 @@ __global__ void __launch_bounds__(kConvThreads) conv_out_kernel(const ConvParams
             for (int k = 0; k + 1 < H; ++k) win[k][v] = win[k + 1][v];
             win[H - 1][v] = xs[i][v];
         }
+        // A one-token row's history was read by this thread alone, so it
+        // writes the new one (the slid window) here and conv_state_kernel
+        // skips the row.
+        if (t1 - t0 == 1 && p.state && !pad) {
+            WT* st = static_cast<WT*>(p.state) + static_cast<int64_t>(slot) * p.st_slot + c0;
+#pragma unroll
+            for (int k = 0; k < H; ++k) store4(st + static_cast<int64_t>(k) * p.st_tok, win[k]);
+        }
     }
 }
 
-// New history of every non-empty, non-padding row: the last W-1 inputs of
-// history ++ row.  Runs after conv_out_kernel on the same stream.
+// New history of every non-padding row of two or more tokens (one-token rows
+// are updated by conv_out_kernel): the last W-1 inputs of history ++ row.
+// Runs after conv_out_kernel on the same stream.
 template <int W, typename WT>
 __global__ void __launch_bounds__(kConvThreads) conv_state_kernel(const ConvParams p) {
     constexpr int H = W - 1;
@@ -142,7 +154,7 @@ __global__ void __launch_bounds__(kConvThreads) conv_state_kernel(const ConvPara
     const int t0 = static_cast<int>(p.offsets[b]), t1 = static_cast<int>(p.offsets[b + 1]);
     const int L = t1 - t0;
     const uint32_t slot = p.slot_idx ? p.slot_idx[b] : static_cast<uint32_t>(b);
-    if (L <= 0 || (p.slot_idx != nullptr && slot == kPadSlot)) return;
+    if (L <= 1 || (p.slot_idx != nullptr && slot == kPadSlot)) return;
     WT* st = static_cast<WT*>(p.state) + static_cast<int64_t>(slot) * p.st_slot + c0;
     const WT* x = static_cast<const WT*>(p.x) + c0;
     float old[H][kConvVec], nw[H][kConvVec];

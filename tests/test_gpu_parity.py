@@ -706,6 +706,29 @@ def test_conv_decode_and_continuity():
     H.assert_close(nz, nz_r, "conv zero-history output")
 
 
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_conv_one_token_rows(W):
+    """One-token rows update their history in the output launch: a bf16
+    decode step, and one-token rows inside 8-token runs (rows of 1, 30, 1, 1,
+    0, 1 tokens, one of them padding) next to longer rows; histories bit-exact
+    against the oracle, untouched slots unchanged."""
+    rng = np.random.Generator(np.random.PCG64(98 + W))
+    d = wl.conv_inputs(rng, [1] * 64, C=512, W=W, slots=80, work_dtype="bf16")
+    out_g, st_g = H.gpu_conv(d)
+    out_r, st_r = _conv_oracle(d)
+    x32 = dict(d, x=wl.bf16_bits_to_f32(d["x"]), conv_state=wl.bf16_bits_to_f32(d["conv_state"]))
+    out_u, _ = _conv_oracle(x32)
+    H.assert_state_close(out_g, out_r, f"conv bf16 decode W={W}", out_u)
+    assert np.array_equal(st_g, st_r), "bf16 decode history"
+    m = wl.conv_inputs(rng, [1, 30, 1, 1, 0, 1], C=256, W=W, slots=9, pad_rows=(3,))
+    assert m["x"].shape[0] >= 4 * 6  # the 8-token-run launch shape
+    out_g, st_g = H.gpu_conv(m)
+    out_r, st_r = _conv_oracle(m)
+    H.assert_close(out_g, out_r, f"conv mixed rows W={W}")
+    assert np.array_equal(st_g, st_r), "mixed rows history"
+    say(f"conv one-token rows W={W}: ok")
+
+
 # ------------------------------------------------------------- degenerate ---
 
 @pytest.mark.parametrize("lengths", [[200, 37, 300, 5, 64, 1], [8, 3, 1, 6, 7, 2]])
