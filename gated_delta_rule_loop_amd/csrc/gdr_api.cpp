@@ -152,7 +152,7 @@ int32_t order_rows(const gdr::LaunchShape& s, const gdr::RecParams& p) {
 }
 
 gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t total_tokens,
-                            int64_t rows) {
+                            int64_t rows, int64_t nv) {
     gdr::LaunchShape s{};
     s.K = static_cast<int>(K);
     s.V = static_cast<int>(V);
@@ -184,7 +184,11 @@ gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t to
             s.chunk = GDR_FUSED_CHUNK;
             s.kg_low = GDR_FUSED_KGLOW;
         } else if (decode) {
-            s.cpl = GDR_DECODE_CPL;
+            // A batch whose decode shape would give 256 waves or fewer (4 rows
+            // at 32 value heads) is latency-bound: narrower tiles spread it
+            // over 4x the waves.
+            const bool tiny = rows * nv * (V / (gdr::kLanesPerRow * GDR_DECODE_CPL)) <= 256;
+            s.cpl = tiny ? GDR_TINY_CPL : GDR_DECODE_CPL;
             s.chunk = GDR_DECODE_CHUNK;
             s.kg_low = GDR_DECODE_KGLOW;
         } else {
@@ -290,7 +294,7 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     if (B * nk > (int64_t{1} << 28))
         return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
 
-    const gdr::LaunchShape s = pick_shape(Entry::Packed, K, V, G, T, B);
+    const gdr::LaunchShape s = pick_shape(Entry::Packed, K, V, G, T, B, nv);
     const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     p.rows = static_cast<int32_t>(B);
     p.nv = nv;
@@ -400,7 +404,7 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
         g_last_error.clear();
         return GDR_OK;
     }
-    gdr::LaunchShape s = pick_shape(Entry::Fold, K, V, G, B, B);
+    gdr::LaunchShape s = pick_shape(Entry::Fold, K, V, G, B, B, nv);
     const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     gdr::FoldParams p{};
     p.rows = static_cast<int32_t>(B);
@@ -544,7 +548,7 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     if (N * H > (int64_t{1} << 28)) return fail(GDR_ERR_INVALID_ARG, "%s: batch too large", fn);
 
     const int64_t G = HV / H;
-    const gdr::LaunchShape s = pick_shape(Entry::Fused, K, V, G, B * T, N);
+    const gdr::LaunchShape s = pick_shape(Entry::Fused, K, V, G, B * T, N, HV);
     const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     p.rows = static_cast<int32_t>(N);
     p.nv = static_cast<int32_t>(HV);

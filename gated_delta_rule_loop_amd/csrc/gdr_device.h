@@ -24,7 +24,8 @@
 //   * S^T k_hat of token t+1 is computed in the same register pass as the
 //     read-out S^T q_hat of token t, so only one pass over the state is made
 //     per token; decay is applied as r = a * (S^T k_hat) on the reduced value.
-//   * no MFMA: the token-serial recurrence is not a dense contraction.#pragma once
+//   * no MFMA: the token-serial recurrence is not a dense contraction.
+#pragma once
 
 #include "gdr_internal.h"
 
@@ -291,7 +292,7 @@ __device__ __forceinline__ void store_state_cols(float* p, const float* s) {
 #pragma unroll
         for (int i = 0; i < CPL; i += 4)
             state_st<true>(f32x4_t{s[i], s[i + 1], s[i + 2], s[i + 3]},
-                     reinterpret_cast<f32x4_t*>(p + i));
+                           reinterpret_cast<f32x4_t*>(p + i));
     } else if constexpr (CPL == 2) {
         state_st<false>(f32x2_t{s[0], s[1]}, reinterpret_cast<f32x2_t*>(p));
     } else {
@@ -301,12 +302,12 @@ __device__ __forceinline__ void store_state_cols(float* p, const float* s) {
 template <int CPL>
 __device__ __forceinline__ void store_state_cols(uint16_t* p, const float* s) {
     if constexpr (CPL == 8) {
-        state_st<true>(u32x4_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]),
-                         pack_bf16x2(s[6], s[7])},
-                 reinterpret_cast<u32x4_t*>(p));
+        state_st<true>(u32x4_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
+                               pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])},
+                       reinterpret_cast<u32x4_t*>(p));
     } else if constexpr (CPL == 4) {
         state_st<false>(u32x2_t{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])},
-                 reinterpret_cast<u32x2_t*>(p));
+                        reinterpret_cast<u32x2_t*>(p));
     } else if constexpr (CPL == 2) {
         state_st<false>(pack_bf16x2(s[0], s[1]), reinterpret_cast<uint32_t*>(p));
     } else {
@@ -1005,6 +1006,7 @@ hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_
     if (s.K == KK && s.V == VV && s.cpl == CC && s.chunk == CH && s.kg_low == KL)    \
         return launch_rec_mode<KK, VV, CC, CH, ST, KL, WT, MODE>(p, s.wpg, stream);
     GDR_REC_CASE(128, 128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
+    GDR_REC_CASE(128, 128, GDR_TINY_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
     GDR_REC_CASE(128, 128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
     GDR_REC_CASE(128, 128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
     GDR_REC_CASE(128, 128, GDR_LONG_CPL, GDR_LONG_CHUNK, GDR_LONG_KGLOW)

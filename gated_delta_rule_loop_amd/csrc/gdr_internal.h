@@ -113,6 +113,9 @@ constexpr int kRollbackPerThread = 8;  // 16-byte vectors per thread
 #ifndef GDR_DECODE_CPL
 #define GDR_DECODE_CPL 8
 #endif
+#ifndef GDR_TINY_CPL
+#define GDR_TINY_CPL 2  // decode batches of at most 256 waves at GDR_DECODE_CPL
+#endif
 #ifndef GDR_DECODE_CHUNK
 #define GDR_DECODE_CHUNK 1
 #endif

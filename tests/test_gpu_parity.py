@@ -798,3 +798,20 @@ def test_longest_first_row_order(rows):
     w["slot_idx"][rows // 3] = wl.PAD_SLOT_U32
     say(f"row order: {rows} rows, {int(lengths.sum())} tokens")
     check_fwd_against_oracle(w, f"row order {rows}")
+
+
+@pytest.mark.parametrize("rows", [1, 4])
+def test_tiny_decode_batch(rows):
+    """Decode batches small enough for the narrow-tile decode shape (1 and 4
+    rows x 32 value heads): against the oracle, and bit for bit the same rows
+    run inside a 64-row batch (the wide decode shape)."""
+    big = wl.decode_step(seed=405, batch=64, slots=128)
+    small = dict(big, qkv=big["qkv"][:rows], decay=big["decay"][:rows], beta=big["beta"][:rows],
+                 slot_idx=big["slot_idx"][:rows].copy(),
+                 row_offsets=big["row_offsets"][:rows + 1].copy())
+    say(f"tiny decode batch: {rows} rows")
+    out_s, st_s = check_fwd_against_oracle(small, f"tiny decode {rows}")
+    out_b, st_b = H.gpu_fwd(big)
+    assert np.array_equal(out_s.view(np.uint32), out_b[:rows].view(np.uint32)), "output bits"
+    sl = small["slot_idx"].astype(np.int64)
+    assert np.array_equal(st_s[sl], st_b[sl]), "state bits"
