@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--only decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,
-                            gdp_v256,gdp_betacols,conv]
+                            gdp_v256,gdp_betacols,conv,decode_small]
                     [--no-cpu-baseline] [--copy-probe MiB]
 
 Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
@@ -136,6 +136,23 @@ def case_decode(torch, gdr, B, wl, rotations):
     alg = state + Bn * 8192 * 4 + Bn * nv * K * 4 + 2 * Bn * nv * 4 + (2 * Bn + 1) * 4
     flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
     return Case("decode_256x1", launches, alg, state, Bn, flops)
+
+
+def case_decode_small(torch, gdr, B, wl, rotations, Bn):
+    """A decode step of Bn one-token rows (small batches: 1, 4, 16, 64), as
+    the 256-row step otherwise.  Event timing of back-to-back launches this
+    short includes the host's launch cost; the kernel trace gives the device
+    time."""
+    launches = []
+    for r in range(rotations):
+        w = wl.decode_step(seed=1001 + 100 * r, batch=Bn)
+        launch, _ = _packed_launch(torch, gdr, B, w)
+        launches.append(launch)
+    nv, K = 32, 128
+    state = Bn * nv * K * K * 2 * 2
+    alg = state + Bn * 8192 * 4 + Bn * nv * K * 4 + 2 * Bn * nv * 4 + (2 * Bn + 1) * 4
+    flops = FLOPS_PER_TOKEN_HEAD_ELEM * Bn * nv * K * K
+    return Case(f"decode_{Bn}x1", launches, alg, state, Bn, flops)
 
 
 def case_decode_bf16(torch, gdr, B, wl, rotations):
@@ -384,7 +401,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--only", default="decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,"
-                                      "gdp_v256,gdp_betacols,conv")
+                                      "gdp_v256,gdp_betacols,conv,decode_small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
@@ -423,6 +440,9 @@ def main():
         cases.extend(case_gdp(torch, gdr, B, wl, 2, V=256))
     if "gdp_betacols" in only:
         cases.extend(case_gdp(torch, gdr, B, wl, 2, beta_cols=True))
+    if "decode_small" in only:
+        for Bn in (1, 4, 16, 64):
+            cases.append(case_decode_small(torch, gdr, B, wl, args.rotations, Bn))
     torch.cuda.synchronize()
 
     results = {}
