@@ -301,6 +301,8 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     p.nk = nk;
     p.G = static_cast<int32_t>(G);
     p.parts = static_cast<int32_t>(units / s.wpg);
+    if (int64_t{p.rows} * p.nk * p.parts > INT32_MAX)
+        return fail(GDR_ERR_INVALID_ARG, "%s: batch too large for one launch", fn);
     p.offsets = as_u32(offsets);
     const char* x = static_cast<const char*>(qkv->data);
     const int64_t es = work == GDR_DTYPE_BF16 ? 2 : 4;
@@ -412,6 +414,8 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
     p.nk = nk;
     p.G = static_cast<int32_t>(G);
     p.parts = static_cast<int32_t>(units / s.wpg);
+    if (int64_t{p.rows} * p.nk * p.parts > INT32_MAX)
+        return fail(GDR_ERR_INVALID_ARG, "%s: batch too large for one launch", fn);
     p.slot_idx = as_u32(slot_idx);
     p.state = recurrent_state->data;
     p.st_slot = recurrent_state->stride[0];
@@ -555,6 +559,8 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     p.nk = static_cast<int32_t>(H);
     p.G = static_cast<int32_t>(G);
     p.parts = static_cast<int32_t>(units / s.wpg);
+    if (int64_t{p.rows} * p.nk * p.parts > INT32_MAX)
+        return fail(GDR_ERR_INVALID_ARG, "%s: batch too large for one launch", fn);
     p.dense_len = static_cast<int32_t>(T);
     p.offsets = as_u32(cu_seqlens);
     p.q = q->data;

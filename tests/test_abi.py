@@ -214,3 +214,14 @@ def test_conv_argument_checks():
     assert call(out=T([10, 64], data=FAKE + 0x1000), x=T([10, 64], data=FAKE + 0x1000)) == -1
     assert call(w=T([64, 4], stride=[1, 64])) == -2               # taps not unit stride
     assert call(x=T([0, 64]), out=T([0, 64], data=FAKE + 0x10000)) == 0  # no tokens: no-op
+
+
+def test_fwd_rejects_a_grid_past_one_launch():
+    """2^26 rows x 4 key heads of 16-token rows at K = V = 128, 8 value heads
+    per key head: the long-row tiling would need 2^33 workgroups."""
+    Bn, T_, nk, nv, K = 1 << 26, 1 << 30, 4, 32, 128
+    a = dict(out=T([T_, nv * K]), state=T([6, nv, K, K], B.GDR_DTYPE_BF16),
+             slot=T([Bn], B.GDR_DTYPE_U32), qkv=T([T_, 2 * nk * K + nv * K]),
+             decay=T([T_, nv]), beta=T([T_, nv]), off=T([Bn + 1], B.GDR_DTYPE_U32))
+    assert call_fwd(a, nv=nv, nk=nk) == -1
+    assert "too large" in B.gdr_last_error_message()
