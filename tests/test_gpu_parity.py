@@ -815,3 +815,43 @@ def test_tiny_decode_batch(rows):
     assert np.array_equal(out_s.view(np.uint32), out_b[:rows].view(np.uint32)), "output bits"
     sl = small["slot_idx"].astype(np.int64)
     assert np.array_equal(st_s[sl], st_b[sl]), "state bits"
+
+
+@pytest.mark.parametrize("lengths", [[1, 17, 3, 24, 2, 40, 5, 41, 9, 2, 1, 3],   # short-row shape
+                                     [17, 40, 33, 41, 24, 16]])                   # long-row shape
+def test_records_across_stages(lengths):
+    """A ring of 40 tokens, so recorded windows span several 8- or 16-token
+    stages: verify output == forward output and the long rows' state ==
+    forward state (bit for bit), short rows' state untouched, and
+    fold(n) == forward over the first n tokens for n across stage
+    boundaries."""
+    ring_len, nk, nv, K = 40, 2, 4, 128
+    nb = len(lengths)
+    w = P.small_packed(406, lengths, nk=nk, nv=nv, K=K, V=K, slots=nb + 3, state_dtype="bf16",
+                       sigma=0.05)
+    w["ring"] = np.zeros((nb + 1, nk, ring_len, wl.ring_record_stride(nv // nk, K, K)),
+                         np.float32)
+    w["ring_slot_idx"] = np.random.Generator(np.random.PCG64(407)).permutation(nb + 1)[:nb].astype(
+        np.uint32)
+    say(f"records across stages: lengths {lengths}, ring_len {ring_len}")
+    out_v, st_v, ring_v = H.gpu_verify(w)
+    out_f, st_f = H.gpu_fwd(w)
+    assert np.array_equal(out_v.view(np.uint32), out_f.view(np.uint32)), "verify output"
+    out_r, _ = oracle_fwd(w)
+    H.assert_close(out_v, out_r, "verify output vs oracle")
+    for b, L in enumerate(lengths):
+        s = w["slot_idx"][b]
+        want = st_f[s] if L > ring_len else w["state"][s]
+        assert np.array_equal(st_v[s], want), f"row {b} state after verify"
+    off = w["row_offsets"].astype(np.int64)
+    for n in (0, 1, 7, 8, 9, 15, 16, 17, 33, 40):
+        acc = np.array([min(n, L) if L <= ring_len else L for L in lengths], np.uint32)
+        folded = H.gpu_fold(w, st_v, ring_v, acc)
+        keep = np.concatenate([np.arange(off[b], off[b] + acc[b]) for b in range(nb)])
+        offs = np.zeros(nb + 1, np.uint32)
+        offs[1:] = np.cumsum(acc)
+        _, st_pre = H.gpu_fwd(dict(w, qkv=w["qkv"][keep], decay=w["decay"][keep],
+                                   beta=w["beta"][keep], row_offsets=offs))
+        for b in range(nb):
+            s = w["slot_idx"][b]
+            assert np.array_equal(folded[s], st_pre[s]), (n, b)
