@@ -817,15 +817,18 @@ def test_tiny_decode_batch(rows):
     assert np.array_equal(st_s[sl], st_b[sl]), "state bits"
 
 
-@pytest.mark.parametrize("lengths", [[1, 17, 3, 24, 2, 40, 5, 41, 9, 2, 1, 3],   # short-row shape
-                                     [17, 40, 33, 41, 24, 16]])                   # long-row shape
-def test_records_across_stages(lengths):
+@pytest.mark.parametrize("lengths,ring_len", [
+    ([1, 17, 3, 24, 2, 40, 5, 41, 9, 2, 1, 3], 40),   # short-row shape
+    ([17, 40, 33, 41, 24, 16], 40),                   # long-row shape
+    ([1, 2, 0, 1, 5, 1], 1),                          # a one-token ring
+])
+def test_records_across_stages(lengths, ring_len):
     """A ring of 40 tokens, so recorded windows span several 8- or 16-token
-    stages: verify output == forward output and the long rows' state ==
-    forward state (bit for bit), short rows' state untouched, and
-    fold(n) == forward over the first n tokens for n across stage
-    boundaries."""
-    ring_len, nk, nv, K = 40, 2, 4, 128
+    stages, and a ring of one token: verify output == forward output and the
+    long rows' state == forward state (bit for bit), short rows' state
+    untouched, and fold(n) == forward over the first n tokens for n across
+    stage boundaries."""
+    nk, nv, K = 2, 4, 128
     nb = len(lengths)
     w = P.small_packed(406, lengths, nk=nk, nv=nv, K=K, V=K, slots=nb + 3, state_dtype="bf16",
                        sigma=0.05)
