@@ -858,3 +858,56 @@ def test_records_across_stages(lengths, ring_len):
         for b in range(nb):
             s = w["slot_idx"][b]
             assert np.array_equal(folded[s], st_pre[s]), (n, b)
+
+
+def test_graph_capture_replays():
+    """The decode forward and the fused GDP update captured in a HIP graph
+    (torch.cuda.CUDAGraph) and replayed three times, the pool reset by eager
+    copies between replays: every replay equals the eager call bit for bit."""
+    import torch
+    import gated_delta_rule_loop_amd as gdr
+    bits = lambda x: x.view(torch.int16) if x.element_size() == 2 else x.view(torch.int32)  # noqa: E731
+    w = wl.decode_step(seed=408, batch=32, slots=64)
+    t = {k: H.dev(w[k]) for k in ("qkv", "decay", "beta", "state", "slot_idx", "row_offsets")}
+    out = torch.empty((32, 32 * 128), device="cuda")
+    gw = wl.gdp_decode(seed=409, batch=16, slots=32)
+    f = {k: H.dev(gw[k]) for k in ("q", "k", "v", "g", "beta", "state", "intermediate_states")}
+    f_idx = H.dev(np.asarray(gw["state_indices"], np.int32))
+    o_f = torch.empty_like(f["v"])
+    init = {"pool": t["state"].clone(), "gdp": f["state"].clone(),
+            "snap": f["intermediate_states"].clone()}
+
+    def reset():
+        t["state"].copy_(init["pool"])
+        f["state"].copy_(init["gdp"])
+        f["intermediate_states"].copy_(init["snap"])
+        out.zero_()
+        o_f.zero_()
+
+    def step():
+        gdr.gdr_recurrence_fwd(out, t["state"], t["slot_idx"], t["qkv"], t["decay"], t["beta"],
+                               t["row_offsets"], num_value_heads=32, num_key_heads=16)
+        gdr.gdr_fused_recurrent_update(f["q"], f["k"], f["v"], g=f["g"], beta=f["beta"],
+                                       scale=gw["scale"], use_qk_l2norm_in_kernel=True,
+                                       state=f["state"], state_indices=f_idx,
+                                       intermediate_states=f["intermediate_states"],
+                                       steps_per_token=gw["steps_per_token"], o=o_f)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [bits(x).clone() for x in (out, t["state"], o_f, f["state"], f["intermediate_states"])]
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    names = ("output", "pool", "GDP output", "GDP state", "snapshots")
+    for r in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [bits(x) for x in (out, t["state"], o_f, f["state"], f["intermediate_states"])]
+        for n, a, b in zip(names, got, eager):
+            assert torch.equal(a, b), f"replay {r}: {n}"
+    say("graph capture: 3 replays bit-identical to eager")
