@@ -844,6 +844,12 @@ struct Rec {
             p, it, c, B, S, scale, w, lane);
     }
 
+    // Stage buffers in LDS: two for the short-row shapes (the next stage is
+    // committed while other waves still read the current one); one for the
+    // long-row shapes, with a second barrier per chunk, so their 32-token
+    // stages fit three workgroups per CU.
+    static constexpr int kStageBufs = KG_LOW ? 1 : 2;
+
     // All chunks of an item whose loaded state is rs and whose chunk-0 inputs
     // are in st; leaves the final state as scale * S.  The state is widened
     // after the first stage is committed, so its loads complete under that
@@ -863,9 +869,12 @@ struct Rec {
         for (int c = 0; c < nch; ++c) {
             const bool next = c + 1 < nch;
             if (next) load_stage<BC>(p, it, c + 1, st, w, lane);
-            run_chunk_mode<MODE>(p, it, c, lds + (c & 1) * BUF, S, scale, w, lane);
+            run_chunk_mode<MODE>(p, it, c, lds + (kStageBufs == 2 ? (c & 1) * BUF : 0), S, scale,
+                                 w, lane);
             if (next) {
-                commit_stage<BC>(p, it, c + 1, st, lds + ((c + 1) & 1) * BUF, w, lane);
+                if constexpr (kStageBufs == 1) __syncthreads();  // the stage has been read
+                commit_stage<BC>(p, it, c + 1, st, lds + (kStageBufs == 2 ? ((c + 1) & 1) * BUF : 0),
+                                 w, lane);
                 __syncthreads();
             }
         }
@@ -934,7 +943,7 @@ constexpr int kMinWaves = C == 1 ? (CPL <= 4 ? 4 : 2) : 1;
 template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
 __global__ void __launch_bounds__(WPG * 64, (kMinWaves<C, CPL>)) rec_kernel(const RecParams p) {
     using Q = Rec<K, V, CPL, C, WPG, ST, KG_LOW, WT>;
-    __shared__ __attribute__((aligned(16))) float lds[2 * Q::template buf<(MODE & kBetaCols) != 0>()];
+    __shared__ __attribute__((aligned(16))) float lds[Q::kStageBufs * Q::template buf<(MODE & kBetaCols) != 0>()];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int kg = Q::row_group(lane);

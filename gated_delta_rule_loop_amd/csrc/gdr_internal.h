@@ -135,7 +135,7 @@ constexpr int kRollbackPerThread = 8;  // 16-byte vectors per thread
 #define GDR_LONG_CPL 1
 #endif
 #ifndef GDR_LONG_CHUNK
-#define GDR_LONG_CHUNK 16
+#define GDR_LONG_CHUNK 32
 #endif
 #ifndef GDR_DECODE_KGLOW
 #define GDR_DECODE_KGLOW false

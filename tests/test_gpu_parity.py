@@ -823,7 +823,7 @@ def test_tiny_decode_batch(rows):
     ([1, 2, 0, 1, 5, 1], 1),                          # a one-token ring
 ])
 def test_records_across_stages(lengths, ring_len):
-    """A ring of 40 tokens, so recorded windows span several 8- or 16-token
+    """A ring of 40 tokens, so recorded windows span several 8- or 32-token
     stages, and a ring of one token: verify output == forward output and the
     long rows' state == forward state (bit for bit), short rows' state
     untouched, and fold(n) == forward over the first n tokens for n across
@@ -847,7 +847,7 @@ def test_records_across_stages(lengths, ring_len):
         want = st_f[s] if L > ring_len else w["state"][s]
         assert np.array_equal(st_v[s], want), f"row {b} state after verify"
     off = w["row_offsets"].astype(np.int64)
-    for n in (0, 1, 7, 8, 9, 15, 16, 17, 33, 40):
+    for n in (0, 1, 7, 8, 9, 16, 17, 31, 32, 33, 40):
         acc = np.array([min(n, L) if L <= ring_len else L for L in lengths], np.uint32)
         folded = H.gpu_fold(w, st_v, ring_v, acc)
         keep = np.concatenate([np.arange(off[b], off[b] + acc[b]) for b in range(nb)])
