@@ -394,6 +394,27 @@ def copy_probe(torch, mib):
     print(json.dumps({"copy_probe_bytes": x.numel(), "launches": 5}))
 
 
+def copy_rate(torch, mib=1024, n=20):
+    """Read + write GB/s of a plain 1 GiB device-to-device copy (torch's copy
+    kernel), timed like the cases: the box's achievable-bandwidth reference."""
+    x = torch.empty(mib * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n):
+        y.copy_(x)
+    e1.record(st)
+    torch.cuda.synchronize()
+    rate = 2 * x.numel() * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return rate
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -475,6 +496,10 @@ def main():
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(c.alg_bytes / s / 1e9 / HBM_PEAK_GBS, 4),
                             "traffic": None if tr is None else tr["bytes_per_launch"]}
+        cp = copy_rate(torch)
+        line["copy_reference"] = {"kind": "torch device copy of 1 GiB, read + write bytes",
+                                  "GBps": round(cp, 1),
+                                  "decode_frac_of_copy": round(c.alg_bytes / s / 1e9 / cp, 4)}
     else:
         line.update({"value": None, "ms_per_step": None, "config": {"workload": args.only}})
     if not args.no_cpu_baseline and "decode" in only:
