@@ -911,3 +911,79 @@ def test_graph_capture_replays():
         for n, a, b in zip(names, got, eager):
             assert torch.equal(a, b), f"replay {r}: {n}"
     say("graph capture: 3 replays bit-identical to eager")
+
+
+def _sweep_case(i):
+    """Seeded random shape i: head dim, GQA, batch, length mix, pool dtype,
+    ring length and ring dtype."""
+    r = np.random.Generator(np.random.PCG64(5000 + i))
+    K = int(r.choice([16, 32, 64, 128, 256]))
+    nk = int(r.choice([1, 2, 4]))
+    nv = nk * int(r.choice([1, 2, 4]))
+    B = int(r.integers(1, 13))
+    mix = r.choice(["decode", "short", "long", "mixed"])
+    if mix == "decode":
+        lengths = r.integers(0, 2, size=B)
+    elif mix == "short":
+        lengths = r.integers(0, 13, size=B)
+    elif mix == "long":
+        lengths = r.integers(16, 70, size=B)
+    else:
+        lengths = np.where(r.random(B) < 0.5, r.integers(0, 5, size=B), r.integers(20, 80, size=B))
+    state_dtype = str(r.choice(["f32", "bf16"]))
+    ring_len = int(r.choice([1, 4, 8, 16]))
+    ring_bf16 = bool(r.random() < 0.5)
+    return K, nk, nv, lengths.astype(np.int64), state_dtype, ring_len, ring_bf16
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shape_sweep(i):
+    """24 seeded random configurations across head dims, GQA ratios, batch
+    sizes, length mixes (every launch profile), pool dtypes and rings: the
+    forward against the oracle; verify output == forward output bit for bit
+    and against the oracle; ring records against the oracle's; the fold
+    against the oracle, and (float32 ring) == forward over the prefix."""
+    K, nk, nv, lengths, sd, ring_len, ring_bf16 = _sweep_case(i)
+    B = len(lengths)
+    say(f"sweep {i}: K={K} nk={nk} nv={nv} lengths={lengths.tolist()} pool={sd} "
+        f"ring_len={ring_len} ring_bf16={ring_bf16}")
+    w = P.small_packed(6000 + i, lengths, nk=nk, nv=nv, K=K, V=K, slots=B + 4, state_dtype=sd,
+                       sigma=0.05)
+    out_f, st_f = check_fwd_against_oracle(w, f"sweep {i} fwd")
+    ring_dt = np.uint16 if ring_bf16 else np.float32
+    w["ring"] = np.zeros((B + 2, nk, ring_len, wl.ring_record_stride(nv // nk, K, K)), ring_dt)
+    w["ring_slot_idx"] = np.random.Generator(np.random.PCG64(7000 + i)).permutation(B + 2)[:B].astype(
+        np.uint32)
+    out_v, st_v, ring_v = H.gpu_verify(w)
+    assert np.array_equal(out_v.view(np.uint32), out_f.view(np.uint32)), "verify output bits"
+    out_r, st_r, ring_r = verify_oracle(w)
+    H.assert_close(out_v, out_r, f"sweep {i} verify output")
+    ring_unr = None
+    if ring_bf16:  # unrounded records: the oracle with a float32 ring
+        ring_unr = verify_oracle(dict(w, ring=np.zeros(w["ring"].shape, np.float32)))[2]
+    H.assert_state_close(ring_v, ring_r, f"sweep {i} ring records", ring_unr)
+    for b, L in enumerate(lengths):
+        s = w["slot_idx"][b]
+        want = st_f[s] if L > ring_len else w["state"][s]
+        assert np.array_equal(st_v[s], want), f"row {b} state after verify"
+    acc = np.array([L // 2 + 1 if 0 < L <= ring_len else L for L in lengths], np.uint32)
+    acc = np.minimum(acc, lengths).astype(np.uint32)
+    folded = H.gpu_fold(w, st_v, ring_v, acc)
+    fold_r = oracle.state_fold(state=st_v, slot_idx=w["slot_idx"], ring=ring_v,
+                               ring_slot_idx=w["ring_slot_idx"], accepted=acc,
+                               num_value_heads=nv, num_key_heads=nk)
+    sl = w["slot_idx"].astype(np.int64)
+    fold_unr = None
+    if sd == "bf16":  # unrounded fold: the oracle on a float32 copy of the pool
+        fold_unr = oracle.state_fold(state=H.f32_pool(st_v), slot_idx=w["slot_idx"], ring=ring_v,
+                                     ring_slot_idx=w["ring_slot_idx"], accepted=acc,
+                                     num_value_heads=nv, num_key_heads=nk)[sl]
+    H.assert_state_close(folded[sl], fold_r[sl], f"sweep {i} fold", fold_unr)
+    if not ring_bf16:
+        off = w["row_offsets"].astype(np.int64)
+        keep = np.concatenate([np.arange(off[b], off[b] + acc[b]) for b in range(B)])
+        offs = np.zeros(B + 1, np.uint32)
+        offs[1:] = np.cumsum(acc)
+        _, st_pre = H.gpu_fwd(dict(w, qkv=w["qkv"][keep], decay=w["decay"][keep],
+                                   beta=w["beta"][keep], row_offsets=offs))
+        assert np.array_equal(folded[sl], st_pre[sl]), "fold == forward prefix"
