@@ -987,3 +987,51 @@ def test_random_shape_sweep(i):
         _, st_pre = H.gpu_fwd(dict(w, qkv=w["qkv"][keep], decay=w["decay"][keep],
                                    beta=w["beta"][keep], row_offsets=offs))
         assert np.array_equal(folded[sl], st_pre[sl]), "fold == forward prefix"
+
+
+_FUSED_DIMS = [(16, 16), (32, 32), (64, 64), (128, 128), (256, 256), (64, 128), (128, 64),
+               (128, 256), (256, 128)]
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_fused_sweep(i):
+    """16 seeded random fused updates: head dims (K != V included), GQA,
+    batch, draft and copy counts (steps_per_token), padding, pool dtype,
+    per-column or head-wise or absent beta, absent log decay, and inputs with
+    or without the DeltaProduct structure: output, pool and snapshots against
+    the oracle; last snapshot == final state; untouched slots unchanged."""
+    r = np.random.Generator(np.random.PCG64(8000 + i))
+    K, V = _FUSED_DIMS[int(r.integers(len(_FUSED_DIMS)))]
+    Hh = int(r.choice([1, 2, 4]))
+    HV = Hh * int(r.choice([1, 2]))
+    Bn, S_draft, M = int(r.integers(1, 9)), int(r.integers(1, 12)), int(r.choice([1, 2, 3]))
+    sd = str(r.choice(["f32", "bf16"]))
+    slots = Bn + 3
+    w = wl.gdp_inputs(r, B=Bn, S_draft=S_draft, M=M, H=Hh, HV=HV, K=K, V=V, slots=slots,
+                      pad_frac=float(r.choice([0.0, 0.3])), state_sigma=0.05, state_dtype=sd,
+                      beta_per_v=bool(r.random() < 0.3))
+    if r.random() < 0.5:  # general inputs: query and decay on every step
+        w["q"] = r.standard_normal(w["q"].shape).astype(np.float32)
+        w["g"] = (-np.logaddexp(0.0, r.standard_normal(w["g"].shape))).astype(np.float32)
+    if r.random() < 0.2:
+        w["g"] = None
+    if r.random() < 0.2:
+        w["beta"] = None
+    say(f"fused sweep {i}: K={K} V={V} H={Hh} HV={HV} B={Bn} T={S_draft * M} spt={M} pool={sd} "
+        f"beta={'none' if w['beta'] is None else w['beta'].ndim} g={'none' if w['g'] is None else 'yes'}")
+    o_g, st_g, inter_g = H.gpu_fused(w)
+    o_r, st_r, inter_r = fused_oracle(w)
+    _, st_u, inter_u = fused_oracle(w, f32=True) if sd == "bf16" else (None, None, None)
+    H.assert_close(o_g, o_r, f"fused sweep {i} output")
+    idx = np.asarray(w["state_indices"])
+    sl = idx[idx >= 0].astype(np.int64)
+    pad = idx < 0
+    assert not o_g[pad].view(np.uint32).any(), "padding rows' output"
+    H.assert_state_close(st_g[sl], st_r[sl], f"fused sweep {i} state",
+                         None if st_u is None else st_u[sl])
+    H.assert_state_close(inter_g[sl], inter_r[sl], f"fused sweep {i} snapshots",
+                         None if inter_u is None else inter_u[sl])
+    assert np.array_equal(inter_g[sl, -1], st_g[sl]), "last snapshot == final state"
+    others = np.setdiff1d(np.arange(slots), sl)
+    assert np.array_equal(st_g[others], w["state"][others])
+    assert np.array_equal(inter_g[others].view(np.uint8), w["intermediate_states"][others].view(np.uint8))
