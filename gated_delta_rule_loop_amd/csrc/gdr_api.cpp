@@ -39,9 +39,21 @@ const char* dtype_name(int32_t d) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Rank, dtype and exact shape check; a shape entry < 0 matches anything.
+// A tensor with a zero extent: its data pointer may be null (an allocator's
+// empty buffer), and nothing is read or written through it.
+bool empty(const gdr_tensor* t) {
+    if (t->ndim < 1 || t->ndim > 5) return false;
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->shape[i] == 0) return true;
+    return false;
+}
+
+// A required tensor that is missing (an empty one may have a null pointer).
+bool missing(const gdr_tensor* t) { return t == nullptr || (t->data == nullptr && !empty(t)); }
+
 int check_tensor(const char* fn, const char* name, const gdr_tensor* t, int ndim,
                  const int64_t* shape, bool allow_f32, bool allow_bf16, bool allow_idx) {
-    if (!present(t)) return fail(GDR_ERR_INVALID_ARG, "%s: %s is null", fn, name);
+    if (missing(t)) return fail(GDR_ERR_INVALID_ARG, "%s: %s is null", fn, name);
     if (t->ndim != ndim)
         return fail(GDR_ERR_INVALID_ARG, "%s: %s must have rank %d (got %d)", fn, name, ndim,
                     t->ndim);
@@ -63,6 +75,7 @@ int check_tensor(const char* fn, const char* name, const gdr_tensor* t, int ndim
 
 // Innermost stride 1, 16-byte base, outer strides multiples of `mult`.
 int check_layout(const char* fn, const char* name, const gdr_tensor* t, int64_t mult) {
+    if (empty(t)) return GDR_OK;  // nothing is read or written through it
     if (t->stride[t->ndim - 1] != 1)
         return fail(GDR_ERR_UNSUPPORTED, "%s: %s must have unit innermost stride", fn, name);
     if (!aligned16(t->data))
@@ -120,7 +133,7 @@ int check_state(const char* fn, const char* name, const gdr_tensor* t, int ndim,
     if (!dims_built(K, V, allow_kv_differ))
         return fail(GDR_ERR_UNSUPPORTED, "%s: head dims K=%lld V=%lld not built (%s)", fn,
                     static_cast<long long>(K), static_cast<long long>(V), kDimsBuilt);
-    if (t->stride[ndim - 1] != 1 || t->stride[ndim - 2] != V)
+    if (!empty(t) && (t->stride[ndim - 1] != 1 || t->stride[ndim - 2] != V))
         return fail(GDR_ERR_UNSUPPORTED, "%s: %s needs a dense K x V block per head", fn, name);
     return check_layout(fn, name, t, t->dtype == GDR_DTYPE_BF16 ? 8 : 4);
 }
@@ -236,7 +249,7 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     const int64_t st_shape[4] = {-1, nv, -1, -1};
     if ((rc = check_state(fn, "recurrent_state", state, 4, st_shape))) return rc;
     const int64_t K = state->shape[2], V = state->shape[3];
-    if (!present(slot_idx)) return fail(GDR_ERR_INVALID_ARG, "%s: slot_idx is null", fn);
+    if (missing(slot_idx)) return fail(GDR_ERR_INVALID_ARG, "%s: slot_idx is null", fn);
     const int64_t B = slot_idx->shape[0];
     if ((rc = check_index_vec(fn, "slot_idx", slot_idx, B))) return rc;
     if ((rc = check_index_vec(fn, "input_row_offsets", offsets, B + 1))) return rc;
@@ -368,7 +381,7 @@ int gdr_recurrence_verify_ring(int32_t num_value_heads, int32_t num_key_heads,
                                const gdr_tensor* ring_slot_idx, float scale, uint32_t flags,
                                void* stream) {
     const char* fn = "gdr_recurrence_verify_ring";
-    if (!present(ring)) return fail(GDR_ERR_INVALID_ARG, "%s: ring is null", fn);
+    if (missing(ring)) return fail(GDR_ERR_INVALID_ARG, "%s: ring is null", fn);
     return packed_walk(fn, num_value_heads, num_key_heads, recurrence_output, recurrent_state,
                        slot_idx, qkv_conv_output, decay_per_token, beta_per_token,
                        input_row_offsets, ring, ring_slot_idx, scale, flags, stream);
@@ -387,7 +400,7 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
     const int64_t st_shape[4] = {-1, nv, -1, -1};
     if ((rc = check_state(fn, "recurrent_state", recurrent_state, 4, st_shape))) return rc;
     const int64_t K = recurrent_state->shape[2], V = recurrent_state->shape[3];
-    if (!present(slot_idx)) return fail(GDR_ERR_INVALID_ARG, "%s: slot_idx is null", fn);
+    if (missing(slot_idx)) return fail(GDR_ERR_INVALID_ARG, "%s: slot_idx is null", fn);
     const int64_t B = slot_idx->shape[0];
     if ((rc = check_index_vec(fn, "slot_idx", slot_idx, B))) return rc;
     if ((rc = check_index_vec(fn, "ring_slot_idx", ring_slot_idx, B))) return rc;
@@ -604,7 +617,7 @@ int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indic
         return rc;
     if (intermediate_states->dtype != state->dtype)
         return fail(GDR_ERR_UNSUPPORTED, "%s: intermediate_states must match the state dtype", fn);
-    if (!present(state_indices)) return fail(GDR_ERR_INVALID_ARG, "%s: state_indices is null", fn);
+    if (missing(state_indices)) return fail(GDR_ERR_INVALID_ARG, "%s: state_indices is null", fn);
     const int64_t N = state_indices->shape[0];
     if ((rc = check_index_vec(fn, "state_indices", state_indices, N))) return rc;
     if ((rc = check_index_vec(fn, "accepted", accepted, N))) return rc;
@@ -651,14 +664,15 @@ int gdr_causal_conv1d(const gdr_tensor* out, const gdr_tensor* x, const gdr_tens
     if ((rc = check_tensor(fn, "out", out, 2, x->shape, true, true, false)) ||
         (rc = check_work_dtype(fn, "out", out, work)) || (rc = check_layout(fn, "out", out, 4)))
         return rc;
-    if (out->data == x->data) return fail(GDR_ERR_INVALID_ARG, "%s: out must not alias x", fn);
+    if (out->data == x->data && !empty(x))
+        return fail(GDR_ERR_INVALID_ARG, "%s: out must not alias x", fn);
     const int64_t wshape[2] = {C, -1};
     if ((rc = check_tensor(fn, "weight", weight, 2, wshape, true, false, false))) return rc;
     const int64_t W = weight->shape[1];
     if (W < 2 || W > 4)
         return fail(GDR_ERR_UNSUPPORTED, "%s: kernel width %lld not built (2, 3, 4)", fn,
                     static_cast<long long>(W));
-    if (weight->stride[1] != 1)
+    if (weight->stride[1] != 1 && !empty(weight))
         return fail(GDR_ERR_UNSUPPORTED, "%s: weight needs unit stride over the taps", fn);
     const int64_t cshape[1] = {C};
     if (present(bias) && ((rc = check_tensor(fn, "bias", bias, 1, cshape, true, false, false))))

@@ -14,7 +14,9 @@
  *     strides in ELEMENTS.  All data pointers are DEVICE pointers owned by the
  *     caller; the library never allocates, frees or synchronises and keeps no
  *     pointer after returning.  A descriptor pointer of NULL, or one whose data
- *     is NULL, means an absent optional argument.
+ *     is NULL, means an absent optional argument.  A required tensor with a
+ *     zero extent may have NULL data (nothing is read or written through it;
+ *     its strides are not checked).
  *   - Work is enqueued on the caller's HIP stream (hipStream_t passed as
  *     void*; NULL is the default stream).  Calls return once the work is
  *     enqueued.

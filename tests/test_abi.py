@@ -214,6 +214,20 @@ def test_conv_argument_checks():
     assert call(out=T([10, 64], data=FAKE + 0x1000), x=T([10, 64], data=FAKE + 0x1000)) == -1
     assert call(w=T([64, 4], stride=[1, 64])) == -2               # taps not unit stride
     assert call(x=T([0, 64]), out=T([0, 64], data=FAKE + 0x10000)) == 0  # no tokens: no-op
+    # empty tensors as an allocator hands them over: null data, any strides
+    assert call(x=T([0, 64], data=0, stride=[1, 7]), out=T([0, 64], data=0)) == 0
+    assert call(x=T([10, 64], data=0)) == -1                      # a non-empty x must exist
+
+
+def test_empty_tensors_may_have_null_data():
+    """A zero-extent required tensor passes with a null pointer (no row to
+    run: the calls return before any launch)."""
+    a = fwd_args(B_=0, T_=0, slot=T([0], B.GDR_DTYPE_U32, data=0),
+                 qkv=T([0, 128], data=0), out=T([0, 64], data=0), decay=T([0, 4], data=0),
+                 beta=T([0, 4], data=0))
+    assert call_fwd(a) == 0, B.gdr_last_error_message()
+    a = fwd_args(slot=T([4], B.GDR_DTYPE_U32, data=0))          # 4 rows need slot_idx
+    assert call_fwd(a) == -1
 
 
 def test_fwd_rejects_a_grid_past_one_launch():

@@ -1035,3 +1035,70 @@ def test_random_fused_sweep(i):
     others = np.setdiff1d(np.arange(slots), sl)
     assert np.array_equal(st_g[others], w["state"][others])
     assert np.array_equal(inter_g[others].view(np.uint8), w["intermediate_states"][others].view(np.uint8))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_conv_sweep(i):
+    """12 seeded random Conv1d calls: channel counts (multiples of 4, a
+    partial last workgroup included), widths 2-4, f32 and bf16, ragged lengths
+    with empty and one-token rows on both launch shapes, padding rows, bias or
+    none, SiLU or none, with or without history: output against the oracle,
+    history bit for bit."""
+    r = np.random.Generator(np.random.PCG64(9000 + i))
+    C = int(r.choice([4, 12, 64, 260, 1028]))
+    W = int(r.choice([2, 3, 4]))
+    work = str(r.choice(["f32", "bf16"]))
+    Bn = int(r.integers(1, 10))
+    lengths = (r.integers(0, 3, size=Bn) if r.random() < 0.5 else r.integers(0, 30, size=Bn))
+    pads = tuple(int(b) for b in np.flatnonzero(r.random(Bn) < 0.2))
+    w = wl.conv_inputs(r, lengths, C=C, W=W, slots=Bn + 2, work_dtype=work, pad_rows=pads)
+    if r.random() < 0.3:
+        w["bias"] = None
+    silu, with_state = bool(r.random() < 0.7), bool(r.random() < 0.8)
+    say(f"conv sweep {i}: C={C} W={W} {work} lengths={lengths.tolist()} pads={pads} "
+        f"bias={w['bias'] is not None} silu={silu} state={with_state}")
+    out_g, st_g = H.gpu_conv(w, silu=silu, with_state=with_state)
+    out_r, st_r = _conv_oracle(w, silu=silu, with_state=with_state)
+    if work == "bf16":
+        x32 = dict(w, x=wl.bf16_bits_to_f32(w["x"]), conv_state=wl.bf16_bits_to_f32(w["conv_state"]))
+        out_u, _ = _conv_oracle(x32, silu=silu, with_state=with_state)
+        H.assert_state_close(out_g, out_r, f"conv sweep {i} output", out_u)
+    else:
+        H.assert_close(out_g, out_r, f"conv sweep {i} output")
+    if with_state:
+        assert np.array_equal(st_g, st_r), "history"
+
+
+def test_all_rows_empty():
+    """Batches whose rows are all empty (zero tokens, so the per-token tensors
+    have no elements and torch hands over null pointers): every entry point
+    accepts them and leaves the pools, ring and histories unchanged."""
+    import torch
+    import gated_delta_rule_loop_amd as gdr
+    w = P.small_packed(410, [0, 0, 0], nk=2, nv=4, K=128, V=128, slots=5, state_dtype="bf16")
+    w["slot_idx"][1] = wl.PAD_SLOT_U32
+    assert w["qkv"].shape[0] == 0
+    out_g, st_g = H.gpu_fwd(w)
+    assert out_g.shape == (0, 512) and np.array_equal(st_g, w["state"])
+    w["ring"] = np.zeros((4, 2, 8, wl.ring_record_stride(2, 128, 128)), np.float32)
+    w["ring_slot_idx"] = np.array([3, 0, 2], np.uint32)
+    _, st_v, ring_v = H.gpu_verify(w)
+    assert np.array_equal(st_v, w["state"]) and not ring_v.any()
+    folded = H.gpu_fold(w, st_v, ring_v, np.zeros(3, np.uint32))
+    assert np.array_equal(folded, w["state"])
+    g = wl.gdp_inputs(np.random.Generator(np.random.PCG64(411)), B=1, S_draft=1, M=1, H=2, HV=4,
+                      K=128, V=128, slots=4, pad_frac=0.0, state_sigma=0.05)
+    q = torch.empty((1, 0, 2, 128), device="cuda")
+    v = torch.empty((1, 0, 4, 128), device="cuda")
+    gl = torch.empty((1, 0, 4), device="cuda")
+    st = H.dev(g["state"])
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")  # three empty sequences
+    idx = torch.tensor([2, -1, 0], dtype=torch.int32, device="cuda")
+    o, _ = gdr.gdr_fused_recurrent_update(q, q, v, g=gl, beta=gl, cu_seqlens=cu, state=st,
+                                          state_indices=idx, use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 4, 128) and np.array_equal(H.host(st), g["state"])
+    c = wl.conv_inputs(np.random.Generator(np.random.PCG64(412)), [0, 0], C=64, W=4, slots=3)
+    out_c, st_c = H.gpu_conv(c)
+    assert out_c.shape == (0, 64) and np.array_equal(st_c, c["conv_state"])
+    say("all rows empty: every entry point a no-op")
