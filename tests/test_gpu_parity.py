@@ -1102,3 +1102,34 @@ def test_all_rows_empty():
     out_c, st_c = H.gpu_conv(c)
     assert out_c.shape == (0, 64) and np.array_equal(st_c, c["conv_state"])
     say("all rows empty: every entry point a no-op")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_rollback_sweep(i):
+    """8 seeded random rollbacks: every built K, V pair, both pool dtypes,
+    1-6 snapshots, accepted counts in [0, I+1], padding, indices and counts
+    as i32 or u32: the pool bit for bit against the oracle's copy."""
+    import torch
+    import gated_delta_rule_loop_amd as gdr
+    r = np.random.Generator(np.random.PCG64(9500 + i))
+    K, V = _FUSED_DIMS[int(r.integers(len(_FUSED_DIMS)))]
+    HV, I, N = int(r.choice([1, 2, 8])), int(r.integers(1, 7)), int(r.integers(1, 20))
+    S = N + 4
+    sd = str(r.choice(["f32", "bf16"]))
+    draw = lambda shape: r.standard_normal(shape).astype(np.float32)  # noqa: E731
+    state = draw((S, HV, K, V))
+    inter = draw((S, I, HV, K, V))
+    if sd == "bf16":
+        state, inter = wl.to_bf16_bits(state), wl.to_bf16_bits(inter)
+    idx = r.permutation(S)[:N].astype(np.int32)
+    idx[r.random(N) < 0.2] = -1
+    acc = r.integers(0, I + 2, size=N).astype(np.int32)
+    as_u32 = bool(r.random() < 0.5)
+    say(f"rollback sweep {i}: K={K} V={V} HV={HV} I={I} N={N} {sd} u32={as_u32}")
+    st_t = H.dev(state)
+    conv = (lambda a: H.dev(a.view(np.uint32))) if as_u32 else (lambda a: H.dev(a))  # noqa: E731
+    gdr.gdr_snapshot_rollback(st_t, conv(idx), H.dev(inter), conv(acc))
+    torch.cuda.synchronize()
+    want = oracle.snapshot_rollback(state=state, state_indices=idx, intermediate_states=inter,
+                                    accepted=acc)
+    assert np.array_equal(H.host(st_t).view(np.uint8), want.view(np.uint8))
