@@ -1133,3 +1133,35 @@ def test_random_rollback_sweep(i):
     want = oracle.snapshot_rollback(state=state, state_indices=idx, intermediate_states=inter,
                                     accepted=acc)
     assert np.array_equal(H.host(st_t).view(np.uint8), want.view(np.uint8))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_bf16_work_sweep(i):
+    """12 seeded random shapes (as the shape sweep) with bf16 per-token inputs
+    and outputs: forward and verify bit for bit the float32 path on the
+    widened inputs with the output rounded once (state and ring records equal),
+    and the forward output against the oracle (tolerance or rounding tie)."""
+    import torch
+    K, nk, nv, lengths, sd, ring_len, ring_bf16 = _sweep_case(100 + i)
+    B = len(lengths)
+    say(f"bf16 work sweep {i}: K={K} nk={nk} nv={nv} lengths={lengths.tolist()} pool={sd}")
+    keys = ("qkv", "decay", "beta")
+    w = wl.bf16_work(P.small_packed(6500 + i, lengths, nk=nk, nv=nv, K=K, V=K, slots=B + 4,
+                                    state_dtype=sd, sigma=0.05))
+    ww = _widened(w, keys)
+    rnd = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    out_b, st_b = H.gpu_fwd(w)
+    out_w, st_w = H.gpu_fwd(ww)
+    assert np.array_equal(out_b, rnd(out_w)) and np.array_equal(st_b, st_w), "forward"
+    out_r, _ = oracle_fwd(w)
+    out_u, _ = oracle_fwd(ww)
+    H.assert_state_close(out_b, out_r, f"bf16 work sweep {i} output", out_u)
+    ring_dt = np.uint16 if ring_bf16 else np.float32
+    for d in (w, ww):
+        d["ring"] = np.zeros((B + 2, nk, ring_len, wl.ring_record_stride(nv // nk, K, K)), ring_dt)
+        d["ring_slot_idx"] = np.arange(B, dtype=np.uint32)[::-1].copy()
+    o_vb, s_vb, r_vb = H.gpu_verify(w)
+    o_vw, s_vw, r_vw = H.gpu_verify(ww)
+    assert np.array_equal(o_vb, out_b), "verify output == forward output"
+    assert np.array_equal(o_vb, rnd(o_vw)) and np.array_equal(s_vb, s_vw), "verify"
+    assert np.array_equal(_bits(r_vb), _bits(r_vw)), "ring records"
