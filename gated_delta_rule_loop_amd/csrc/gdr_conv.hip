@@ -1,6 +1,7 @@
 // gfx950 kernels of the Pass-1 causal Conv1d that produces the recurrence's
-// packed qkv_conv_output (page "gated_delta_recurrence_fwd_gpu", Args: the
-// conv output "from Pass 1"; the page names the step without specifying it).
+// packed qkv_conv_output (page "gated_delta_recurrence_fwd_gpu", Args: the input
+// is the output of a first-pass convolution that the page names without
+// specifying it).
 //
 // Reading implemented (the same as the CPU oracle's): a causal depthwise
 // convolution of width W along the token axis of each ragged row, optional

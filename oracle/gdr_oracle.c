@@ -39,7 +39,7 @@
  *   - bf16 state stores round to nearest even, once per store; loads widen.
  *   - Slot index 0xFFFFFFFF (-1 as int32) is a padding request in every
  *     entry: zero output, no state, ring or snapshot access.
- *   - Ring record (verify page: "the record the fold needs"):
+ *   - Ring record (verify page: each token's record holds what the fold uses):
  *       [ k_hat (K) | u of value head h*G+m, m < G (G*V) | a of those heads (G) ]
  *     so the fold needs no norm, exp or reduction.
  *   - Fold count: per-row accepted[b]; 0 or > RING_LEN leaves the state alone.
@@ -483,7 +483,7 @@ void oracle_fwd_output_shape(int64_t total_seq_len, int64_t nv, int64_t V, int64
 
 /*
  * [gdp] intermediate_states: entry [slot, i] is the state after draft token i,
- * "so verification can roll the recurrence back to any accepted prefix".
+ * kept so that a verifier can return the recurrence to any accepted prefix.
  * For request n with slot idx = state_indices[n] (>= 0) and accepted[n] = a
  * draft tokens, 1 <= a <= int_tokens: state[idx] <- intermediate[idx, a-1].
  * a == 0, a > int_tokens and padding requests (-1) leave the state alone (the
