@@ -745,37 +745,62 @@ struct Rec {
         }
         int snap_i = SNAP ? tc / p.spt : 0;
 
+        // In the spread form (multi-token stages, row groups high) the
+        // retrieval stays spread: this lane holds the totals of columns
+        // vc + scol(i), computes u and u / scale for those columns only, and
+        // broadcasts u / scale to the CPL columns it updates.  The same
+        // operations on the same values per column as the column-by-column
+        // path, so the same bits.
+        const int r16 = lane >> 4;
+        auto scol = [&](int i) { return (CPL == 2 ? (r16 & 1) : r16) + 4 * i; };
+        const bool spread_lead = (lane & 8) == 0 && (CPL != 2 || lane < 32);
         float kr[R];
         read_rows<R>(B + OFF_K, kg, kr);
-        float x[CPL];  // S^T k_hat of the current token, before the scale
+        float x[CPL];                 // S^T k_hat of the current token, before the scale
+        float xs[kSpread<CPL>];       // the same, spread (kSpreadOut)
         dot_rows<R, CPL>(S, kr, x);
-        sum_cols_all(x);
+        if constexpr (kSpreadOut) sum_cols_spread<CPL>(x, xs);
+        else sum_cols_all(x);
 
         for (int tau = 0; tau < Lc; ++tau) {
             const float a = B[OFF_A + w * C + tau];
-            float vv[CPL], be[CPL];
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) vv[cc] = B[OFF_V + w * VTOT + tau * BV + vc + cc];
-            if constexpr (BC) {
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) be[cc] = B[OFF_BV + w * VTOT + tau * BV + vc + cc];
-            } else {
-                const float b = B[OFF_B + w * C + tau];
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) be[cc] = b;
-            }
+            const float b = BC ? 1.0f : B[OFF_B + w * C + tau];
             // r = S_{t-1}^T k_hat with this token's decay: (scale * a) * x
             const float cn = scale * a;
-            float u[CPL];
+            float u[CPL];                 // column-by-column path
+            float us[CPL];                // u / scale for the lane's columns
+            float u_s[kSpread<CPL>];      // spread path: u of the spread columns
+            if constexpr (kSpreadOut) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) u[cc] = be[cc] * (vv[cc] - cn * x[cc]);
+                for (int i = 0; i < kSpread<CPL>; ++i) {
+                    const int cc = scol(i);
+                    const float vv = B[OFF_V + w * VTOT + tau * BV + vc + cc];
+                    const float be = BC ? B[OFF_BV + w * VTOT + tau * BV + vc + cc] : b;
+                    u_s[i] = be * (vv - cn * xs[i]);
+                }
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const float vv = B[OFF_V + w * VTOT + tau * BV + vc + cc];
+                    const float be = BC ? B[OFF_BV + w * VTOT + tau * BV + vc + cc] : b;
+                    u[cc] = be * (vv - cn * x[cc]);
+                }
+            }
             scale = decay_step<R, CPL>(S, cn);
             const float rho = __builtin_amdgcn_rcpf(scale);
+            if constexpr (kSpreadOut) {
+                float us_s[kSpread<CPL>];
+#pragma unroll
+                for (int i = 0; i < kSpread<CPL>; ++i) us_s[i] = u_s[i] * rho;
+                spread_to_all<CPL>(us_s, us);
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) us[cc] = u[cc] * rho;
+            }
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
-                const float us = u[cc] * rho;
 #pragma unroll
-                for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us, S[ri][cc]);
+                for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us[cc], S[ri][cc]);
             }
 
             float qr[R];
@@ -785,20 +810,19 @@ struct Rec {
             if (C > 1 && tau + 1 < Lc) {
                 read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
                 dot_rows<R, CPL>(S, kr, x);
-                sum_cols_all(x);
+                if constexpr (kSpreadOut) sum_cols_spread<CPL>(x, xs);
+                else sum_cols_all(x);
             }
             if constexpr (kSpreadOut) {
                 // totals spread over the rows: lanes of even row groups store
                 // their row's column(s)
                 float y[kSpread<CPL>];
                 sum_cols_spread<CPL>(o, y);
-                const int r = lane >> 4;
-                if ((lane & 8) == 0 && (CPL != 2 || lane < 32)) {
-                    const int col = CPL == 2 ? (r & 1) : r;
+                if (spread_lead) {
 #pragma unroll
                     for (int i = 0; i < kSpread<CPL>; ++i) {
                         const float val = scale * y[i];
-                        store_cols<1>(outp + col + 4 * i, &val);
+                        store_cols<1>(outp + scol(i), &val);
                     }
                 }
             } else {
@@ -813,7 +837,12 @@ struct Rec {
             outp += p.o_tok;
             if (REC && it.record) {
                 const int64_t ru = rec + K + it.m * V + it.j0;
-                if (kg == 0) {
+                if constexpr (kSpreadOut) {  // u of the spread columns
+                    if (spread_lead) {
+#pragma unroll
+                        for (int i = 0; i < kSpread<CPL>; ++i) ring_put(p, ru + scol(i), u_s[i]);
+                    }
+                } else if (kg == 0) {
                     if (p.ring_bf16)
                         store_cols<CPL>(static_cast<uint16_t*>(p.ring) + ru, u);
                     else
