@@ -44,7 +44,9 @@ extern "C" {
 #endif
 
 #define GDR_OK 0
-#define GDR_ERR_INVALID_ARG (-1) /* null, rank, shape or stride mismatch */
+#define GDR_ERR_INVALID_ARG (-1) /* null, rank, shape or stride mismatch, or a
+                                    batch whose launch grid would exceed 2^31-1
+                                    workgroups */
 #define GDR_ERR_UNSUPPORTED (-2) /* dtype, head dim or layout not built  */
 #define GDR_ERR_HIP (-3)         /* the HIP runtime refused the launch    */
 
