@@ -897,10 +897,17 @@ struct Rec {
         const int nch = (it.L + C - 1) / C;
         for (int c = 0; c < nch; ++c) {
             const bool next = c + 1 < nch;
-            if (next) load_stage<BC>(p, it, c + 1, st, w, lane);
+            // The long-row and one-token shapes issue the next stage's loads
+            // before this stage's tokens; the short-row shapes after them, so
+            // the loaded registers are not held through the token loop (which
+            // lets the 4-column shape run 4 waves per SIMD; their rows mostly
+            // fit one stage anyway).
+            constexpr bool kLateLoads = !KG_LOW && C > 1;
+            if (!kLateLoads && next) load_stage<BC>(p, it, c + 1, st, w, lane);
             run_chunk_mode<MODE>(p, it, c, lds + (kStageBufs == 2 ? (c & 1) * BUF : 0), S, scale,
                                  w, lane);
             if (next) {
+                if (kLateLoads) load_stage<BC>(p, it, c + 1, st, w, lane);
                 if constexpr (kStageBufs == 1) __syncthreads();  // the stage has been read
                 commit_stage<BC>(p, it, c + 1, st, lds + (kStageBufs == 2 ? ((c + 1) & 1) * BUF : 0),
                                  w, lane);
@@ -965,12 +972,14 @@ __device__ int ordered_row(const uint32_t* off, int B, int rank, uint32_t* scrat
 }
 
 // One work item per workgroup.
-// One-token stages are the HBM-bound decode shape: ask for 4 waves per SIMD.
-template <int C, int CPL>
-constexpr int kMinWaves = C == 1 ? (CPL <= 4 ? 4 : 2) : 1;
+// Waves per SIMD asked of the register allocator: the one-token (HBM-bound
+// decode) stages 4, or 2 at 8 columns per lane; the short-row shapes of at most
+// 4 columns at K <= 128 4 (verify window: -3.6%); the rest as many as fit.
+template <int K, int C, int CPL, bool KG_LOW>
+constexpr int kMinWaves = C == 1 ? (CPL <= 4 ? 4 : 2) : (!KG_LOW && K <= 128 && CPL <= 4 ? 4 : 1);
 
 template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
-__global__ void __launch_bounds__(WPG * 64, (kMinWaves<C, CPL>)) rec_kernel(const RecParams p) {
+__global__ void __launch_bounds__(WPG * 64, (kMinWaves<K, C, CPL, KG_LOW>)) rec_kernel(const RecParams p) {
     using Q = Rec<K, V, CPL, C, WPG, ST, KG_LOW, WT>;
     __shared__ __attribute__((aligned(16))) float lds[Q::kStageBufs * Q::template buf<(MODE & kBetaCols) != 0>()];
     const int lane = threadIdx.x & 63;
