@@ -1069,9 +1069,7 @@ hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_
     if constexpr ((MODE & 3) != kVerify) {  // K != V: the fused update only
         GDR_REC_CASE(64, 128, 8, 8, false)
         GDR_REC_CASE(64, 128, 2, 16, true)
-        GDR_REC_CASE(128, 64, 4, 8, false)
         GDR_REC_CASE(128, 64, 1, 16, true)
-        GDR_REC_CASE(128, 256, 4, 8, false)
         GDR_REC_CASE(128, 256, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
         GDR_REC_CASE(128, 64, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
         GDR_REC_CASE(128, 256, 1, 16, true)
