@@ -936,9 +936,9 @@ def _sweep_case(i):
     return K, nk, nv, lengths.astype(np.int64), state_dtype, ring_len, ring_bf16
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(64))
 def test_random_shape_sweep(i):
-    """24 seeded random configurations across head dims, GQA ratios, batch
+    """64 seeded random configurations across head dims, GQA ratios, batch
     sizes, length mixes (every launch profile), pool dtypes and rings: the
     forward against the oracle; verify output == forward output bit for bit
     and against the oracle; ring records against the oracle's; the fold
@@ -993,9 +993,9 @@ _FUSED_DIMS = [(16, 16), (32, 32), (64, 64), (128, 128), (256, 256), (64, 128), 
                (128, 256), (256, 128)]
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(48))
 def test_random_fused_sweep(i):
-    """16 seeded random fused updates: head dims (K != V included), GQA,
+    """48 seeded random fused updates: head dims (K != V included), GQA,
     batch, draft and copy counts (steps_per_token), padding, pool dtype,
     per-column or head-wise or absent beta, absent log decay, and inputs with
     or without the DeltaProduct structure: output, pool and snapshots against
@@ -1037,9 +1037,9 @@ def test_random_fused_sweep(i):
     assert np.array_equal(inter_g[others].view(np.uint8), w["intermediate_states"][others].view(np.uint8))
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(32))
 def test_random_conv_sweep(i):
-    """12 seeded random Conv1d calls: channel counts (multiples of 4, a
+    """32 seeded random Conv1d calls: channel counts (multiples of 4, a
     partial last workgroup included), widths 2-4, f32 and bf16, ragged lengths
     with empty and one-token rows on both launch shapes, padding rows, bias or
     none, SiLU or none, with or without history: output against the oracle,
@@ -1104,9 +1104,9 @@ def test_all_rows_empty():
     say("all rows empty: every entry point a no-op")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(24))
 def test_random_rollback_sweep(i):
-    """8 seeded random rollbacks: every built K, V pair, both pool dtypes,
+    """24 seeded random rollbacks: every built K, V pair, both pool dtypes,
     1-6 snapshots, accepted counts in [0, I+1], padding, indices and counts
     as i32 or u32: the pool bit for bit against the oracle's copy."""
     import torch
@@ -1135,9 +1135,9 @@ def test_random_rollback_sweep(i):
     assert np.array_equal(H.host(st_t).view(np.uint8), want.view(np.uint8))
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(32))
 def test_random_bf16_work_sweep(i):
-    """12 seeded random shapes (as the shape sweep) with bf16 per-token inputs
+    """32 seeded random shapes (as the shape sweep) with bf16 per-token inputs
     and outputs: forward and verify bit for bit the float32 path on the
     widened inputs with the output rounded once (state and ring records equal),
     and the forward output against the oracle (tolerance or rounding tie)."""
