@@ -427,8 +427,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: the recurrence has no cross-GPU step in this "
-              "build; run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one MI355X: every (sequence, value head) recurrence is "
+              "independent and has no cross-GPU step; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

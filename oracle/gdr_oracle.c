@@ -32,8 +32,7 @@
  * the fwd page fixes), one scalar operation at a time, with contraction off
  * (built with -ffp-contract=off) so that no fused multiply-add appears.
  *
- * Readings of points the pages leave open (each one is listed with its reason
- * in the design notes of this repository):
+ * Readings of points the pages leave open:
  *   - L2 norm: x * (1 / sqrt(sum x^2 + eps)) with eps = 1e-6.
  *   - GQA: value head hv reads key head hv / (nv / nk).
  *   - bf16 state stores round to nearest even, once per store; loads widen.
