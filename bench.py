@@ -347,6 +347,23 @@ def time_case(torch, case, steps, warmup):
     return ms / steps, wall
 
 
+def launch_spread(torch, case, n):
+    """p10 / median / p90 of single launches (one HIP event pair around each, on
+    the launch stream), taken after the timed region; the reported rate comes
+    from the back-to-back timed region, not from these."""
+    stream = torch.cuda.current_stream()
+    m = len(case.launches)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        case.launches[i % m]()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return [round(us[n // 10], 2), round(us[n // 2], 2), round(us[(9 * n) // 10], 2)]
+
+
 def summarize(case, ms_per_launch):
     s = ms_per_launch * 1e-3
     d = {"us_per_launch": round(ms_per_launch * 1e3, 2),
@@ -473,6 +490,8 @@ def main():
         ms, wall = time_case(torch, c, steps, args.warmup if c.name != "prefill_8x4096" else 2)
         results[c.name] = summarize(c, ms)
         results[c.name]["launches_timed"] = steps
+        results[c.name]["single_launch_us_p10_p50_p90"] = launch_spread(
+            torch, c, min(steps, 100 if c.name != "prefill_8x4096" else 5))
         print(f"# {c.name}: {json.dumps(results[c.name])}", file=sys.stderr, flush=True)
         if c.name == "decode_256x1":
             head = (c, ms, steps)
