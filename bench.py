@@ -490,6 +490,9 @@ def main():
         ms, wall = time_case(torch, c, steps, args.warmup if c.name != "prefill_8x4096" else 2)
         results[c.name] = summarize(c, ms)
         results[c.name]["launches_timed"] = steps
+        if "max_len" in results[c.name]:  # the token-serial critical path of the longest row
+            results[c.name]["ns_per_step_of_longest_row"] = round(
+                ms * 1e6 / results[c.name]["max_len"], 1)
         results[c.name]["single_launch_us_p10_p50_p90"] = launch_spread(
             torch, c, min(steps, 100 if c.name != "prefill_8x4096" else 5))
         print(f"# {c.name}: {json.dumps(results[c.name])}", file=sys.stderr, flush=True)
