@@ -20,9 +20,16 @@
  *   - Work is enqueued on the caller's HIP stream (hipStream_t passed as
  *     void*; NULL is the default stream).  Calls return once the work is
  *     enqueued.
- *   - The innermost dimension of every float tensor must have stride 1 and a
- *     16-byte aligned base; other strides are free (multiples of 4 elements
- *     for float32 data, 8 for bfloat16 state).
+ *   - Layout.  Tensors read or written with vector accesses need a unit
+ *     innermost stride and a 16-byte aligned base: state pools, snapshots
+ *     and initial/final states (each head's K x V block dense), rings,
+ *     qkv_conv_output, recurrence_output, the fused update's q, k, v, o and
+ *     per-column beta, and the Conv1d's x, out and history.  Their outer
+ *     strides must keep 16-byte rows (multiples of 4 elements for float32
+ *     and of 8 for bfloat16), except the fused q and k (any outer stride)
+ *     and the Conv1d tensors (multiples of 4 elements in either dtype).
+ *     Per-token gates (decay, beta, g, head-wise beta) take any strides;
+ *     index vectors of more than one element must be contiguous.
  *   - Return value: GDR_OK, or a negative GDR_ERR_* code with a message
  *     available from gdr_last_error_message() (thread-local).  Argument
  *     checks happen on the host before anything is enqueued; a failed check
