@@ -1165,3 +1165,45 @@ def test_random_bf16_work_sweep(i):
     assert np.array_equal(o_vb, out_b), "verify output == forward output"
     assert np.array_equal(o_vb, rnd(o_vw)) and np.array_equal(s_vb, s_vw), "verify"
     assert np.array_equal(_bits(r_vb), _bits(r_vw)), "ring records"
+
+
+def test_element_offsets_past_2_to_31():
+    """Maximum-size indexing: 6,000 rows of 1,000 tokens with one key and one
+    value head at K = V = 128 and bf16 per-token tensors, so qkv holds 2.3e9
+    elements and the last rows start past element 2^31 (byte offsets past
+    2^32).  Every row gets the same inputs and the same initial state, so every
+    row must give the same output and final-state bits; the last row is also
+    checked against the oracle."""
+    import torch
+
+    import gated_delta_rule_loop_amd as gdr
+    rows, L = 6000, 1000
+    base = wl.bf16_work(P.small_packed(8800, [L], nk=1, nv=1, K=128, V=128, slots=1,
+                                       state_dtype="f32", sigma=0.05))
+    conv = base["qkv"].shape[1]
+    assert (rows - 1) * L * conv > 2**31
+    say(f"offsets past 2^31: {rows} rows x {L} tokens, qkv [{rows * L}, {conv}] bf16")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    qkv = bf(base["qkv"]).repeat(rows, 1)
+    decay = bf(base["decay"]).repeat(rows, 1)
+    beta = bf(base["beta"]).repeat(rows, 1)
+    state = torch.from_numpy(base["state"]).cuda().repeat(rows, 1, 1, 1)
+    slots = torch.arange(rows, dtype=torch.int32, device="cuda")
+    offs = torch.arange(rows + 1, dtype=torch.int32, device="cuda") * L
+    out = torch.full((rows * L, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdr.gdr_recurrence_fwd(out, state, slots, qkv, decay, beta, offs, num_value_heads=1,
+                           num_key_heads=1)
+    torch.cuda.synchronize()
+    ob = out.view(torch.int16).view(rows, L * 128)
+    sb = state.view(torch.int32).view(rows, -1)
+    assert bool((ob == ob[:1]).all()), "every row's output bits equal row 0's"
+    assert bool((sb == sb[:1]).all()), "every row's final state equals row 0's"
+    del qkv, decay, beta
+    last_out = ob[-1].cpu().numpy().view(np.uint16).reshape(L, 128)
+    last_state = state[-1:].cpu().numpy()
+    out_r, st_r = oracle_fwd(base)
+    out_u, _ = oracle_fwd(_widened(base, ("qkv", "decay", "beta")))
+    H.assert_state_close(last_out, out_r, "last row output (bf16)", out_u)
+    H.assert_close(last_state, st_r, "last row final state")
+    say("offsets past 2^31: all rows bit-identical, last row within tolerance of the oracle")
