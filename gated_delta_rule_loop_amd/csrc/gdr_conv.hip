@@ -183,7 +183,7 @@ hipError_t launch_conv_w(const ConvParams& p, hipStream_t stream) {
     const unsigned cblocks = (p.C / kConvVec + kConvThreads - 1) / kConvThreads;
     // runs of 8 tokens when rows average 4 or more tokens, else one token
     if (p.T >= 4 * p.B) {
-        const dim3 grid(cblocks, (p.T + 7) / 8);
+        const dim3 grid(cblocks, static_cast<unsigned>((int64_t{p.T} + 7) / 8));
         hipLaunchKernelGGL((conv_out_kernel<W, WT, 8>), grid, dim3(kConvThreads), 0, stream, p);
     } else {
         const dim3 grid(cblocks, p.T);

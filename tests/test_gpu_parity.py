@@ -1207,3 +1207,45 @@ def test_element_offsets_past_2_to_31():
     H.assert_state_close(last_out, out_r, "last row output (bf16)", out_u)
     H.assert_close(last_state, st_r, "last row final state")
     say("offsets past 2^31: all rows bit-identical, last row within tolerance of the oracle")
+
+
+def test_conv_element_offsets_past_2_to_31():
+    """Maximum-size indexing for the Conv1d: 6,000 rows of 1,000 tokens at
+    C = 384 in bf16 (2.3e9 elements of x; the last rows start past element
+    2^31), every row with the same inputs and history: all rows' outputs and
+    new histories bit-identical, the last row against the oracle (history bit
+    for bit)."""
+    import torch
+
+    import gated_delta_rule_loop_amd as gdr
+    rows, L, C, W = 6000, 1000, 384, 4
+    base = wl.conv_inputs(np.random.Generator(np.random.PCG64(8810)), [L], C=C, W=W, slots=1,
+                          work_dtype="bf16")
+    base["slot_idx"] = np.zeros(1, np.uint32)
+    assert (rows - 1) * L * C > 2**31
+    say(f"conv offsets past 2^31: {rows} rows x {L} tokens x {C} channels, bf16")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    x = bf(base["x"]).repeat(rows, 1)
+    hist = bf(base["conv_state"]).repeat(rows, 1, 1)
+    weight = torch.from_numpy(base["weight"]).cuda()
+    bias = torch.from_numpy(base["bias"]).cuda()
+    slots = torch.arange(rows, dtype=torch.int32, device="cuda")
+    offs = torch.arange(rows + 1, dtype=torch.int32, device="cuda") * L
+    out = gdr.gdr_causal_conv1d(x, weight, offs, bias=bias, conv_state=hist, slot_idx=slots,
+                                silu=True)
+    torch.cuda.synchronize()
+    del x
+    ob = out.view(torch.int16).view(rows, L * C)
+    hb = hist.view(torch.int16).view(rows, -1)
+    assert bool((ob == ob[:1]).all()), "every row's output bits equal row 0's"
+    assert bool((hb == hb[:1]).all()), "every row's new history equals row 0's"
+    last_out = ob[-1].cpu().numpy().view(np.uint16).reshape(L, C)
+    last_hist = hb[-1:].cpu().numpy().view(np.uint16).reshape(1, W - 1, C)
+    out_r, st_r = _conv_oracle(base, silu=True, with_state=True)
+    x32 = dict(base, x=wl.bf16_bits_to_f32(base["x"]),
+               conv_state=wl.bf16_bits_to_f32(base["conv_state"]))
+    out_u, _ = _conv_oracle(x32, silu=True, with_state=True)
+    H.assert_state_close(last_out, out_r, "conv last row output (bf16)", out_u)
+    assert np.array_equal(last_hist, st_r), "conv last row history"
+    say("conv offsets past 2^31: all rows bit-identical, last row against the oracle")
