@@ -1249,3 +1249,46 @@ def test_conv_element_offsets_past_2_to_31():
     H.assert_state_close(last_out, out_r, "conv last row output (bf16)", out_u)
     assert np.array_equal(last_hist, st_r), "conv last row history"
     say("conv offsets past 2^31: all rows bit-identical, last row against the oracle")
+
+
+def test_fused_element_offsets_past_2_to_31():
+    """Maximum-size indexing for the fused update: 6,000 requests of 1,000
+    steps, H = 1, HV = 4, K = V = 128, bf16 work, so v and o hold 3.1e9
+    elements and the last requests start past element 2^31.  Every request has
+    the same inputs and cached state: all outputs and final states bit-identical,
+    the last request against the oracle."""
+    import torch
+
+    import gated_delta_rule_loop_amd as gdr
+    rows, T, HV = 6000, 1000, 4
+    base = wl.bf16_work(wl.gdp_inputs(np.random.Generator(np.random.PCG64(8820)), B=1,
+                                      S_draft=T, M=1, H=1, HV=HV, K=128, V=128, slots=1,
+                                      pad_frac=0.0, state_sigma=0.05, state_dtype="f32"))
+    base["state_indices"] = np.zeros(1, np.int32)
+    base["intermediate_states"] = None
+    assert (rows - 1) * T * HV * 128 > 2**31
+    say(f"fused offsets past 2^31: {rows} requests x {T} steps, v [{rows}, {T}, {HV}, 128] bf16")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    rep = lambda t: t.repeat(rows, *([1] * (t.dim() - 1)))  # noqa: E731
+    q, k, v = rep(bf(base["q"])), rep(bf(base["k"])), rep(bf(base["v"]))
+    g, beta = rep(bf(base["g"])), rep(bf(base["beta"]))
+    state = rep(torch.from_numpy(base["state"]).cuda())
+    idx = torch.arange(rows, dtype=torch.int32, device="cuda")
+    o, _ = gdr.gdr_fused_recurrent_update(q, k, v, g=g, beta=beta, scale=base["scale"],
+                                          use_qk_l2norm_in_kernel=True, state=state,
+                                          state_indices=idx)
+    torch.cuda.synchronize()
+    del q, k, v, g, beta
+    ob = o.view(torch.int16).view(rows, -1)
+    sb = state.view(torch.int32).view(rows, -1)
+    assert bool((ob == ob[:1]).all()), "every request's output bits equal request 0's"
+    assert bool((sb == sb[:1]).all()), "every request's final state equals request 0's"
+    last_o = ob[-1].cpu().numpy().view(np.uint16).reshape(1, T, HV, 128)
+    last_state = state[-1:].cpu().numpy()
+    o_r, st_r, _ = oracle.fused_recurrent_update(**base)
+    wide = _widened(base, ("q", "k", "v", "g", "beta"))
+    o_u, _, _ = oracle.fused_recurrent_update(**wide)
+    H.assert_state_close(last_o, o_r, "fused last request output (bf16)", o_u)
+    H.assert_close(last_state, st_r, "fused last request final state")
+    say("fused offsets past 2^31: all requests bit-identical, last request against the oracle")
