@@ -18,6 +18,9 @@
  *            parameters.
  * The Pass-1 causal Conv1d that produces the fwd page's qkv_conv_output is
  * only named there; oracle_causal_conv1d states the reading it implements.
+ * Parity unpinned against the pages for that reading (nothing on them fixes
+ * the step); its arithmetic is pinned by exact delays, numpy's convolve and
+ * split-call continuity.
  *
  * The recurrence (per sequence and value head, a K x V state S carried token
  * by token; the pages call it the gated delta rule and describe the state as
@@ -34,13 +37,15 @@
  *
  * Readings of points the pages leave open:
  *   - L2 norm: x * (1 / sqrt(sum x^2 + eps)) with eps = 1e-6.
- *   - GQA: value head hv reads key head hv / (nv / nk).
+ *   - GQA: value head hv reads key head hv / (nv / nk).  Parity unpinned
+ *     against the pages (a convention; pinned only by replicated heads).
  *   - bf16 state stores round to nearest even, once per store; loads widen.
  *   - Slot index 0xFFFFFFFF (-1 as int32) is a padding request in every
  *     entry: zero output, no state, ring or snapshot access.
  *   - Ring record (verify page: each token's record holds what the fold uses):
  *       [ k_hat (K) | u of value head h*G+m, m < G (G*V) | a of those heads (G) ]
- *     so the fold needs no norm, exp or reduction.
+ *     so the fold needs no norm, exp or reduction.  Parity unpinned for the
+ *     layout (the page fixes only its size's dependence on nv / nk).
  *   - Fold count: per-row accepted[b]; 0 or > RING_LEN leaves the state alone.
  */
 #include <math.h>
