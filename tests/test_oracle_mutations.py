@@ -12,6 +12,21 @@ from tests import oracle_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gdr_oracle.c")
 
+# The decay and the retrieval of one step, as written in the oracle (for the
+# mutation that retrieves from the undecayed state).
+_DECAY = """    for (int i = 0; i < K; ++i)
+        for (int j = 0; j < V; ++j)
+            S[i * V + j] = a * S[i * V + j];
+"""
+_RETRIEVAL = """    for (int j = 0; j < V; ++j) {
+        float r = 0.0f;
+        for (int i = 0; i < K; ++i)
+            r = r + S[i * V + j] * khat[i];
+        float b = beta_per_v ? beta[j] : beta[0];
+        u[j] = b * (v[j] - r);
+    }
+"""
+
 # (name, original text, planted text)
 MUTATIONS = [
     ("delta_sign", "u[j] = b * (v[j] - r);", "u[j] = b * (v[j] + r);"),
@@ -44,6 +59,14 @@ MUTATIONS = [
     ("conv_silu_sign", "y = y / (1.0f + expf(-y));", "y = y / (1.0f + expf(y));"),
     ("offsets_shifted", "const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];",
      "const int64_t t0 = row_offsets[b] + (b > 0), t1 = row_offsets[b + 1];"),
+    ("readout_before_write", "acc = acc + S[i * V + j] * qhat[i];",
+     "acc = acc + (S[i * V + j] - khat[i] * u[j]) * qhat[i];"),
+    ("retrieval_before_decay", _DECAY + "\n" + _RETRIEVAL, _RETRIEVAL + "\n" + _DECAY),
+    ("q_not_normalised", "        oracle_l2norm(K, q, qhat);\n",
+     "        for (int i = 0; i < K; ++i)\n            qhat[i] = q[i];\n"),
+    ("log_decay_not_exponentiated", "const float a = g ? expf(g[f * HV + hv]) : 1.0f;",
+     "const float a = g ? g[f * HV + hv] : 1.0f;"),
+    ("fold_u_of_head_0", "rec + K + (int64_t)m * V + j", "rec + K + j"),
 ]
 
 
