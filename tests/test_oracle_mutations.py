@@ -67,6 +67,18 @@ MUTATIONS = [
     ("log_decay_not_exponentiated", "const float a = g ? expf(g[f * HV + hv]) : 1.0f;",
      "const float a = g ? g[f * HV + hv] : 1.0f;"),
     ("fold_u_of_head_0", "rec + K + (int64_t)m * V + j", "rec + K + j"),
+    ("snapshot_step_not_sequence_local", "const int64_t step = f - f0 + 1;",
+     "const int64_t step = f + 1;"),
+    ("initial_state_ignored",
+     "oracle_load_block(initial_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);",
+     "for (int64_t e = 0; e < kv; ++e) S[e] = 0.0f;"),
+    ("conv_history_ignored",
+     "window[j] = conv_state[((int64_t)slot * H + (H + (s - t0))) * C + c];",
+     "window[j] = 0.0f;"),
+    ("conv_short_row_drops_old_history",
+     "hist[i] = conv_state[((int64_t)slot * H + (L + i)) * C + c];", "hist[i] = 0.0f;"),
+    ("conv_bias_dropped",
+     "float y = bias ? bias[c] : 0.0f;", "float y = 0.0f;"),
 ]
 
 
