@@ -773,6 +773,38 @@ def test_extreme_decays(lengths):
         assert np.array_equal(folded[s].view(np.uint32), st_pre[s].view(np.uint32)), b
 
 
+@pytest.mark.parametrize("L", [3, 40])
+def test_degenerate_tokens(L):
+    """Degenerate tokens of the update, L2 norm on, on the short-row (L = 3)
+    and long-row (L = 40) shapes: zero keys (k_hat = 0, so no write and
+    r = 0: the state only decays), zero queries (every output 0), and a token
+    with beta = 1 followed by the same key with beta = 0, a = 1 and q = k, which
+    reads back exactly what was written (scale * v).  Against the oracle too."""
+    nk, nv, K, V = 2, 4, 128, 128
+    w = wl.packed_inputs(np.random.Generator(np.random.PCG64(420 + L)), [L, L, L], nk=nk,
+                         nv=nv, K=K, V=V, slots=6, state_dtype="f32", state_sigma=0.3)
+    off = w["row_offsets"].astype(np.int64)
+    qc, kc = slice(0, nk * K), slice(nk * K, 2 * nk * K)
+    w["qkv"][off[0]:off[1], kc] = 0.0          # row 0: zero keys
+    w["qkv"][off[1]:off[2], qc] = 0.0          # row 1: zero queries
+    t0 = off[2]                                # row 2: write, then read the same key back
+    w["beta"][t0] = 1.0
+    w["qkv"][t0 + 1, kc] = w["qkv"][t0, kc]
+    w["qkv"][t0 + 1, qc] = w["qkv"][t0, kc]
+    w["beta"][t0 + 1] = 0.0
+    w["decay"][t0 + 1] = 1.0
+    say(f"degenerate tokens, L={L}")
+    out, st = check_fwd_against_oracle(w, f"degenerate tokens L={L}")
+    S0 = w["state"]
+    a = np.prod(w["decay"][off[0]:off[1]].astype(np.float64), axis=0)   # [nv]
+    want = (a[:, None, None] * S0[w["slot_idx"][0]].astype(np.float64)).astype(np.float32)
+    H.assert_close(st[w["slot_idx"][0]], want, "zero keys: the state only decays", rel=1e-5)
+    assert not out[off[1]:off[2]].any(), "zero queries: every output is 0"
+    sc = oracle.default_scale(K)
+    v0 = w["qkv"][t0, 2 * nk * K:]
+    H.assert_close(out[t0 + 1], sc * v0, "beta = 1 then the same key reads v back", rel=1e-5)
+
+
 def test_large_decode_batch():
     """2048 one-token rows (8,192 workgroups) against the oracle: index
     arithmetic of large grids, every row checked."""
