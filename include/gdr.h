@@ -200,10 +200,10 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
  *   state_indices     [N] i32|u32, -1 = padding request (zero output, no
  *                     state or snapshot access)
  *   intermediate_states [S, T/steps_per_token, HV, K, V], same dtype as state,
- *                     or absent; needs state.  Entry [slot, i] receives the
- *                     state after draft token i, i.e. after
- *                     (i+1)*steps_per_token steps; steps past shape[1] are not
- *                     snapshotted.
+ *                     or absent; needs state.  Snapshot i of a slot is
+ *                     the state once (i+1)*steps_per_token steps of the
+ *                     request are done (draft token i complete); steps past
+ *                     shape[1] snapshots are not recorded.
  *   steps_per_token   >= 1
  *   o                 [B, T, HV, V] work (out)
  */
@@ -218,9 +218,10 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
 /*
  * gdr_snapshot_rollback - roll each request's cached state back to the
  * snapshot taken after its last accepted draft token.
- * Source: page "core.ssm.ops.gdp.fused_recurrent" (intermediate_states: entry
- * [slot, i] holds the state after draft token i, so that verification can
- * roll the recurrence back to any accepted prefix).
+ * Source: page "core.ssm.ops.gdp.fused_recurrent" (update() parameters,
+ * intermediate_states: the snapshots exist so that a verifier that accepts
+ * only some of the draft tokens can restore the state at the last accepted
+ * one).
  *
  *   state               [S, HV, K, V] bf16|f32 cache (in/out)
  *   state_indices       [N] i32|u32 cache slot per request, -1 = padding

@@ -25,6 +25,22 @@ _lib = None
 
 PAD_SLOT = 0xFFFFFFFF
 
+_ENTRY_POINTS = ("oracle_recurrence_fwd_threads", "oracle_recurrence_verify_ring_threads",
+                 "oracle_state_fold", "oracle_fused_recurrent_update_threads",
+                 "oracle_snapshot_rollback", "oracle_causal_conv1d")
+
+
+def default_threads() -> int:
+    """Threads for the work-item farm: OMP_NUM_THREADS if set, else the CPUs
+    this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return max(1, os.cpu_count() or 1)
+
 
 def _load():
     global _lib
@@ -33,9 +49,7 @@ def _load():
             from . import build as _build  # noqa: PLC0415
             _build.build()
         _lib = ctypes.CDLL(_LIB_PATH)
-        for name in ("oracle_recurrence_fwd", "oracle_recurrence_verify_ring",
-                     "oracle_state_fold", "oracle_fused_recurrent_update",
-                     "oracle_snapshot_rollback", "oracle_causal_conv1d"):
+        for name in _ENTRY_POINTS:
             getattr(_lib, name).restype = ctypes.c_int
     return _lib
 
@@ -51,9 +65,7 @@ class using_library:
         global _lib
         self.saved = _load()
         lib = ctypes.CDLL(self.path)
-        for name in ("oracle_recurrence_fwd", "oracle_recurrence_verify_ring",
-                     "oracle_state_fold", "oracle_fused_recurrent_update",
-                     "oracle_snapshot_rollback", "oracle_causal_conv1d"):
+        for name in _ENTRY_POINTS:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -118,12 +130,14 @@ def default_scale(K: int) -> float:
 
 
 def recurrence_fwd(*, qkv, decay, beta, state, slot_idx, row_offsets, num_value_heads,
-                   num_key_heads, scale=None, l2norm=True):
+                   num_key_heads, scale=None, l2norm=True, threads=1):
     """Ragged slot-indexed forward ("gated_delta_recurrence_fwd_gpu").
 
     qkv, decay and beta share the work dtype: float32, or uint16 bf16 bits
     (verify page, work_dtype), which widen exactly; the output is then rounded
-    to bf16 once.  Returns (out [T, nv*V] of the work dtype, state_after)."""
+    to bf16 once.  threads > 1 runs the independent (row, value head) items
+    on that many threads (same results).  Returns (out [T, nv*V] of the work
+    dtype, state_after)."""
     lib = _load()
     st, bf = _state_copy(state)
     K, V = st.shape[2], st.shape[3]
@@ -134,12 +148,37 @@ def recurrence_fwd(*, qkv, decay, beta, state, slot_idx, row_offsets, num_value_
     T = qkv.shape[0]
     out = np.zeros((T, num_value_heads * V), dtype=np.float32)
     sc = default_scale(K) if scale is None else scale
-    rc = lib.oracle_recurrence_fwd(
+    rc = lib.oracle_recurrence_fwd_threads(
         B, num_value_heads, num_key_heads, K, V, _p(off), _p(sl), _p(qkv), _p(decay), _p(beta),
-        bf, _p(st), ctypes.c_int64(st.shape[0]), _p(out), ctypes.c_float(sc), int(l2norm))
+        bf, _p(st), ctypes.c_int64(st.shape[0]), _p(out), ctypes.c_float(sc), int(l2norm),
+        int(threads))
     if rc != 0:
         raise ValueError(f"oracle_recurrence_fwd failed: {rc}")
     return (bf16_round(out) if work_bf16 else out), st
+
+
+def recurrence_fwd_into(*, out, state, qkv, decay, beta, slot_idx, row_offsets,
+                        num_value_heads, num_key_heads, scale=None, l2norm=True, threads=1):
+    """recurrence_fwd writing into the caller's arrays: out [T, nv*V] float32
+    and the pool state (float32 or uint16 bf16 bits), both C-contiguous and
+    updated in place; float32 per-token inputs only.  For timing the oracle
+    itself (no copy of the pool per call)."""
+    lib = _load()
+    if state.dtype not in (np.float32, np.uint16) or out.dtype != np.float32:
+        raise TypeError("state must be float32 or uint16, out float32")
+    for a in (qkv, decay, beta):
+        if a.dtype != np.float32:
+            raise TypeError("per-token inputs must be float32")
+    K, V = state.shape[2], state.shape[3]
+    off = np.ascontiguousarray(row_offsets, dtype=np.uint32)
+    sl = np.ascontiguousarray(slot_idx, dtype=np.uint32)
+    sc = default_scale(K) if scale is None else scale
+    rc = lib.oracle_recurrence_fwd_threads(
+        sl.shape[0], num_value_heads, num_key_heads, K, V, _p(off), _p(sl), _p(qkv),
+        _p(decay), _p(beta), int(state.dtype == np.uint16), _p(state),
+        ctypes.c_int64(state.shape[0]), _p(out), ctypes.c_float(sc), int(l2norm), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_recurrence_fwd failed: {rc}")
 
 
 def ring_record_elements(group: int, K: int, V: int) -> int:
@@ -149,11 +188,12 @@ def ring_record_elements(group: int, K: int, V: int) -> int:
 
 
 def recurrence_verify_ring(*, qkv, decay, beta, state, slot_idx, row_offsets, num_value_heads,
-                           num_key_heads, ring, ring_slot_idx, scale=None, l2norm=True):
+                           num_key_heads, ring, ring_slot_idx, scale=None, l2norm=True,
+                           threads=1):
     """Verify window with ring ("gated_delta_recurrence_verify_ring_gpu").
 
     ring: [ring_rows, nk, ring_len, rec_stride], float32 or uint16 (bf16 bits),
-    copied.  Work dtype as recurrence_fwd.
+    copied.  Work dtype and threads as recurrence_fwd.
     Returns (out, state_after, ring_after)."""
     lib = _load()
     st, bf = _state_copy(state)
@@ -166,11 +206,11 @@ def recurrence_verify_ring(*, qkv, decay, beta, state, slot_idx, row_offsets, nu
     B, T = sl.shape[0], qkv.shape[0]
     out = np.zeros((T, num_value_heads * V), dtype=np.float32)
     sc = default_scale(K) if scale is None else scale
-    rc = lib.oracle_recurrence_verify_ring(
+    rc = lib.oracle_recurrence_verify_ring_threads(
         B, num_value_heads, num_key_heads, K, V, _p(off), _p(sl), _p(qkv), _p(decay), _p(beta),
         bf, _p(st), ctypes.c_int64(st.shape[0]), _p(out), ctypes.c_float(sc), int(l2norm),
         _p(rg), rbf, _p(rsl), ctypes.c_int64(rg.shape[0]), rg.shape[2],
-        ctypes.c_int64(rg.shape[3]))
+        ctypes.c_int64(rg.shape[3]), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_recurrence_verify_ring failed: {rc}")
     return (bf16_round(out) if work_bf16 else out), st, rg
@@ -203,7 +243,7 @@ def state_fold(*, state, slot_idx, ring, ring_slot_idx, accepted, num_value_head
 def fused_recurrent_update(*, q, k, v, g=None, beta=None, scale=None, initial_state=None,
                            output_final_state=False, use_qk_l2norm_in_kernel=False,
                            cu_seqlens=None, state=None, state_indices=None,
-                           intermediate_states=None, steps_per_token=1):
+                           intermediate_states=None, steps_per_token=1, threads=1):
     """Fused recurrent update ("core.ssm.ops.gdp.fused_recurrent").
 
     q, k [B, T, H, K]; v [B, T, HV, V]; g, beta [B, T, HV] (beta may be
@@ -212,7 +252,8 @@ def fused_recurrent_update(*, q, k, v, g=None, beta=None, scale=None, initial_st
     q, k, v, g, beta share the work dtype likewise, and o is of that dtype.
     Returns (o, final_state, intermediate_after): final_state is the updated
     pool copy when a pool is given, the dense final state when requested, else
-    None; intermediate_after is the updated snapshot copy or None."""
+    None; intermediate_after is the updated snapshot copy or None.  threads as
+    recurrence_fwd (items are (sequence, value head) pairs)."""
     lib = _load()
     (q, k, v, g, beta), work_bf16 = _work((q, k, v, g, beta))
     B, T, H, K = q.shape
@@ -233,12 +274,12 @@ def fused_recurrent_update(*, q, k, v, g=None, beta=None, scale=None, initial_st
     idx = None if state_indices is None else np.ascontiguousarray(state_indices, dtype=np.int32)
     o = np.zeros((B, T, HV, V), dtype=np.float32)
     sc = default_scale(K) if scale is None else scale
-    rc = lib.oracle_fused_recurrent_update(
+    rc = lib.oracle_fused_recurrent_update_threads(
         B, T, H, HV, K, V, _p(q), _p(k), _p(v), _p(g), _p(beta), beta_per_v,
         ctypes.c_float(sc), int(use_qk_l2norm_in_kernel), _p(cu), N, sbf, _p(st),
         ctypes.c_int64(0 if st is None else st.shape[0]), _p(idx), _p(init), _p(final),
         _p(inter), ctypes.c_int64(0 if inter is None else inter.shape[1]), int(steps_per_token),
-        _p(o))
+        _p(o), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_fused_recurrent_update failed: {rc}")
     return (bf16_round(o) if work_bf16 else o), (st if st is not None else final), inter

@@ -14,7 +14,7 @@ SRC = os.path.join(HERE, "gdr_oracle.c")
 LIB = os.path.join(HERE, "libgdr_oracle.so")
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-strict-aliasing",
-          "-Wall", "-Wextra", "-shared", "-fPIC"]
+          "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread"]
 
 
 def build(verbose: bool = False) -> str:

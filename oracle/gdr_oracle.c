@@ -49,6 +49,8 @@
  *   - Fold count: per-row accepted[b]; 0 or > RING_LEN leaves the state alone.
  */
 #include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -188,8 +190,9 @@ static void oracle_step(int K, int V, float* S, const float* khat, const float* 
 }
 
 /* Fetch and optionally normalise q_t, k_t of key head h from the packed conv
- * output row ([fwd] Args, qkv_conv_output: Q in channels [0, key_dim), K in
- * [key_dim, 2*key_dim), V in [2*key_dim, 2*key_dim + value_dim)). */
+ * output row ([fwd] Args, qkv_conv_output: the queries of all key heads come
+ * first, then the keys, then the values, so q of key head h starts at channel
+ * h*K, k at nk*K + h*K and v of value head hv at 2*nk*K + hv*V). */
 static void oracle_packed_qk(const float* row, int nk, int K, int h, int l2norm,
                              float* qhat, float* khat)
 {
@@ -206,76 +209,166 @@ static void oracle_packed_qk(const float* row, int nk, int K, int h, int l2norm,
     }
 }
 
+/* ------------------------------------------------- work-item farm ------ */
+
+/*
+ * Every (sequence, value head) pair is an independent recurrence: it reads and
+ * writes only its own state block, output columns and ring elements (slots
+ * are distinct by precondition).  The walks below are therefore written as
+ * one function per work item, and oracle_farm runs items 0..items-1 either in
+ * order on the calling thread (threads <= 1) or spread over a few threads
+ * that take the next item from a shared counter.  Either way each item runs
+ * the same single-threaded code, so the results are identical.
+ */
+typedef int (*oracle_item_fn)(const void* args, int64_t item);
+
+typedef struct {
+    oracle_item_fn fn;
+    const void* args;
+    int64_t items;
+    atomic_llong next;
+    atomic_int rc;
+} oracle_farm_state;
+
+static void* oracle_farm_worker(void* arg)
+{
+    oracle_farm_state* f = (oracle_farm_state*)arg;
+    for (;;) {
+        const int64_t i = atomic_fetch_add(&f->next, 1);
+        if (i >= f->items || atomic_load(&f->rc) != 0)
+            break;
+        const int rc = f->fn(f->args, i);
+        if (rc != 0) {
+            int zero = 0;
+            atomic_compare_exchange_strong(&f->rc, &zero, rc);
+        }
+    }
+    return NULL;
+}
+
+static int oracle_farm(oracle_item_fn fn, const void* args, int64_t items, int threads)
+{
+    if (threads <= 1 || items <= 1) {
+        for (int64_t i = 0; i < items; ++i) {
+            const int rc = fn(args, i);
+            if (rc != 0)
+                return rc;
+        }
+        return 0;
+    }
+    if (threads > 256)
+        threads = 256;
+    oracle_farm_state f;
+    f.fn = fn;
+    f.args = args;
+    f.items = items;
+    atomic_init(&f.next, 0);
+    atomic_init(&f.rc, 0);
+    pthread_t tid[256];
+    int started = 0;
+    for (int t = 0; t < threads; ++t) {
+        if (pthread_create(&tid[t], NULL, oracle_farm_worker, &f) != 0)
+            break;
+        ++started;
+    }
+    if (started == 0)
+        oracle_farm_worker(&f);
+    for (int t = 0; t < started; ++t)
+        pthread_join(tid[t], NULL);
+    return atomic_load(&f.rc);
+}
+
 /* -------------------------------------------- ragged forward and verify --- */
 
 /*
- * Shared walker for the [fwd] and [verify] entries.  All arrays contiguous:
+ * Arguments of the [fwd] and [verify] walks.  All arrays contiguous:
  *   row_offsets [B+1], slot_idx [B], qkv [T, 2*nk*K + nv*V],
  *   decay, beta [T, nv], state [max_slots, nv, K, V], out [T, nv*V],
- *   ring [ring_rows, nk, ring_len, rec_stride] (verify only), ring_slot_idx [B].
+ *   ring [ring_rows, nk, ring_len, rec_stride] (verify only, else NULL),
+ *   ring_slot_idx [B].
  * Verify ([verify] summary): same outputs as the forward; a row no longer than
  * ring_len writes one record per token and leaves the state alone; a longer
  * row writes no record and stores its state like the forward.
  */
-static int oracle_walk(int B, int nv, int nk, int K, int V, const uint32_t* row_offsets,
-                       const uint32_t* slot_idx, const float* qkv, const float* decay,
-                       const float* beta, int state_bf16, void* state, int64_t max_slots,
-                       float* out, float scale, int l2norm, void* ring, int ring_bf16,
-                       const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
-                       int64_t rec_stride)
+typedef struct {
+    int B, nv, nk, K, V;
+    const uint32_t* row_offsets;
+    const uint32_t* slot_idx;
+    const float* qkv;
+    const float* decay;
+    const float* beta;
+    int state_bf16;
+    void* state;
+    int64_t max_slots;
+    float* out;
+    float scale;
+    int l2norm;
+    void* ring;
+    int ring_bf16;
+    const uint32_t* ring_slot_idx;
+    int64_t ring_rows;
+    int ring_len;
+    int64_t rec_stride;
+} oracle_walk_args;
+
+/* One work item of the walk: row b, value head hv (item = b * nv + hv). */
+static int oracle_walk_item(const void* args, int64_t item)
 {
-    if (nk <= 0 || nv % nk != 0)
-        return -1;
+    const oracle_walk_args* w = (const oracle_walk_args*)args;
+    const int nv = w->nv, nk = w->nk, K = w->K, V = w->V;
+    const int b = (int)(item / nv);
+    const int hv = (int)(item % nv);
     const int G = nv / nk;
     const int64_t conv_dim = 2 * (int64_t)nk * K + (int64_t)nv * V;
     const int64_t kv = (int64_t)K * V;
+    const uint32_t* row_offsets = w->row_offsets;
+    float* out = w->out;
+    void* ring = w->ring;
+    const int ring_len = w->ring_len;
+
+    const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];
+    const uint32_t slot = w->slot_idx[b];
+    const int h = hv / G;
+    const int m = hv % G;
+    if (slot == ORACLE_PAD_SLOT) {
+        for (int64_t t = t0; t < t1; ++t)
+            for (int j = 0; j < V; ++j)
+                out[t * nv * V + (int64_t)hv * V + j] = 0.0f;
+        return 0;
+    }
+    if ((int64_t)slot >= w->max_slots)
+        return -2;
+    const int64_t soff = ((int64_t)slot * nv + hv) * kv;
+    const int use_ring = ring != NULL && (t1 - t0) <= ring_len;
+    const uint32_t rrow = ring ? w->ring_slot_idx[b] : 0;
+    if (ring && use_ring && (int64_t)rrow >= w->ring_rows)
+        return -2;
+
     float* S = (float*)malloc(sizeof(float) * (size_t)kv);
     float* qhat = (float*)malloc(sizeof(float) * (size_t)K);
     float* khat = (float*)malloc(sizeof(float) * (size_t)K);
     float* u = (float*)malloc(sizeof(float) * (size_t)V);
-
-    for (int b = 0; b < B; ++b) {
-        const int64_t t0 = row_offsets[b], t1 = row_offsets[b + 1];
-        const uint32_t slot = slot_idx[b];
-        for (int hv = 0; hv < nv; ++hv) {
-            const int h = hv / G;
-            const int m = hv % G;
-            if (slot == ORACLE_PAD_SLOT) {
-                for (int64_t t = t0; t < t1; ++t)
-                    for (int j = 0; j < V; ++j)
-                        out[t * nv * V + (int64_t)hv * V + j] = 0.0f;
-                continue;
-            }
-            if ((int64_t)slot >= max_slots)
-                return -2;
-            const int64_t soff = ((int64_t)slot * nv + hv) * kv;
-            const int use_ring = ring != NULL && (t1 - t0) <= ring_len;
-            const uint32_t rrow = ring ? ring_slot_idx[b] : 0;
-            if (ring && use_ring && (int64_t)rrow >= ring_rows)
-                return -2;
-            oracle_load_block(state, state_bf16, soff, kv, S);
-            for (int64_t t = t0; t < t1; ++t) {
-                const float* row = qkv + t * conv_dim;
-                oracle_packed_qk(row, nk, K, h, l2norm, qhat, khat);
-                const float* v = row + 2 * (int64_t)nk * K + (int64_t)hv * V;
-                const float a = decay[t * nv + hv];
-                const float bt = beta[t * nv + hv];
-                oracle_step(K, V, S, khat, qhat, v, a, &bt, 0, scale,
-                            out + t * nv * V + (int64_t)hv * V, u);
-                if (use_ring) {
-                    const int64_t rec = (((int64_t)rrow * nk + h) * ring_len + (t - t0)) * rec_stride;
-                    if (m == 0)
-                        for (int i = 0; i < K; ++i)
-                            oracle_ring_put(ring, ring_bf16, rec + i, khat[i]);
-                    for (int j = 0; j < V; ++j)
-                        oracle_ring_put(ring, ring_bf16, rec + K + (int64_t)m * V + j, u[j]);
-                    oracle_ring_put(ring, ring_bf16, rec + K + (int64_t)G * V + m, a);
-                }
-            }
-            if (t1 > t0 && !use_ring)
-                oracle_store_block(state, state_bf16, soff, kv, S);
+    oracle_load_block(w->state, w->state_bf16, soff, kv, S);
+    for (int64_t t = t0; t < t1; ++t) {
+        const float* row = w->qkv + t * conv_dim;
+        oracle_packed_qk(row, nk, K, h, w->l2norm, qhat, khat);
+        const float* v = row + 2 * (int64_t)nk * K + (int64_t)hv * V;
+        const float a = w->decay[t * nv + hv];
+        const float bt = w->beta[t * nv + hv];
+        oracle_step(K, V, S, khat, qhat, v, a, &bt, 0, w->scale,
+                    out + t * nv * V + (int64_t)hv * V, u);
+        if (use_ring) {
+            const int64_t rec = (((int64_t)rrow * nk + h) * ring_len + (t - t0)) * w->rec_stride;
+            if (m == 0)
+                for (int i = 0; i < K; ++i)
+                    oracle_ring_put(ring, w->ring_bf16, rec + i, khat[i]);
+            for (int j = 0; j < V; ++j)
+                oracle_ring_put(ring, w->ring_bf16, rec + K + (int64_t)m * V + j, u[j]);
+            oracle_ring_put(ring, w->ring_bf16, rec + K + (int64_t)G * V + m, a);
         }
     }
+    if (t1 > t0 && !use_ring)
+        oracle_store_block(w->state, w->state_bf16, soff, kv, S);
     free(S);
     free(qhat);
     free(khat);
@@ -283,18 +376,57 @@ static int oracle_walk(int B, int nv, int nk, int K, int V, const uint32_t* row_
     return 0;
 }
 
+static int oracle_walk(const oracle_walk_args* w, int threads)
+{
+    if (w->nk <= 0 || w->nv % w->nk != 0)
+        return -1;
+    return oracle_farm(oracle_walk_item, w, (int64_t)w->B * w->nv, threads);
+}
+
 /* [fwd]: slot-indexed ragged forward; the state of slot slot_idx[b] is read,
- * advanced over the row and written back in place. */
+ * advanced over the row and written back in place.  threads > 1 spreads the
+ * independent (row, value head) items over that many threads. */
+int oracle_recurrence_fwd_threads(int B, int nv, int nk, int K, int V,
+                                  const uint32_t* row_offsets, const uint32_t* slot_idx,
+                                  const float* qkv, const float* decay, const float* beta,
+                                  int state_bf16, void* state, int64_t max_slots, float* out,
+                                  float scale, int l2norm, int threads)
+{
+    const oracle_walk_args w = {B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta,
+                                state_bf16, state, max_slots, out, scale, l2norm,
+                                NULL, 0, NULL, 0, 0, 0};
+    return oracle_walk(&w, threads);
+}
+
 int oracle_recurrence_fwd(int B, int nv, int nk, int K, int V, const uint32_t* row_offsets,
                           const uint32_t* slot_idx, const float* qkv, const float* decay,
                           const float* beta, int state_bf16, void* state, int64_t max_slots,
                           float* out, float scale, int l2norm)
 {
-    return oracle_walk(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta, state_bf16,
-                       state, max_slots, out, scale, l2norm, NULL, 0, NULL, 0, 0, 0);
+    return oracle_recurrence_fwd_threads(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay,
+                                         beta, state_bf16, state, max_slots, out, scale, l2norm,
+                                         1);
 }
 
-/* [verify]: the forward over a verify window, recording a float32 ring. */
+/* [verify]: the forward over a verify window, recording a float32 (or bf16)
+ * ring. */
+int oracle_recurrence_verify_ring_threads(int B, int nv, int nk, int K, int V,
+                                          const uint32_t* row_offsets, const uint32_t* slot_idx,
+                                          const float* qkv, const float* decay,
+                                          const float* beta, int state_bf16, void* state,
+                                          int64_t max_slots, float* out, float scale,
+                                          int l2norm, void* ring, int ring_bf16,
+                                          const uint32_t* ring_slot_idx, int64_t ring_rows,
+                                          int ring_len, int64_t rec_stride, int threads)
+{
+    if (rec_stride < (int64_t)K + (int64_t)(nv / (nk > 0 ? nk : 1)) * (V + 1))
+        return -1;
+    const oracle_walk_args w = {B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta,
+                                state_bf16, state, max_slots, out, scale, l2norm,
+                                ring, ring_bf16, ring_slot_idx, ring_rows, ring_len, rec_stride};
+    return oracle_walk(&w, threads);
+}
+
 int oracle_recurrence_verify_ring(int B, int nv, int nk, int K, int V,
                                   const uint32_t* row_offsets, const uint32_t* slot_idx,
                                   const float* qkv, const float* decay, const float* beta,
@@ -303,11 +435,10 @@ int oracle_recurrence_verify_ring(int B, int nv, int nk, int K, int V,
                                   const uint32_t* ring_slot_idx, int64_t ring_rows, int ring_len,
                                   int64_t rec_stride)
 {
-    if (rec_stride < (int64_t)K + (int64_t)(nv / (nk > 0 ? nk : 1)) * (V + 1))
-        return -1;
-    return oracle_walk(B, nv, nk, K, V, row_offsets, slot_idx, qkv, decay, beta, state_bf16,
-                       state, max_slots, out, scale, l2norm, ring, ring_bf16, ring_slot_idx,
-                       ring_rows, ring_len, rec_stride);
+    return oracle_recurrence_verify_ring_threads(B, nv, nk, K, V, row_offsets, slot_idx, qkv,
+                                                 decay, beta, state_bf16, state, max_slots, out,
+                                                 scale, l2norm, ring, ring_bf16, ring_slot_idx,
+                                                 ring_rows, ring_len, rec_stride, 1);
 }
 
 /* [verify] (fold paragraphs): advance the live state of row b over its first
@@ -372,19 +503,138 @@ int oracle_state_fold(int B, int nv, int nk, int K, int V, const uint32_t* slot_
  *   output, nothing else touched), or NULL; then initial_state [N, HV, K, V]
  *   (NULL = zeros) seeds the walk and final_state [N, HV, K, V] (or NULL)
  *   receives the end state.
- *   intermediate [num_slots, int_tokens, HV, K, V] or NULL: entry [slot, i]
- *   receives the state after draft token i, i.e. after (i+1)*steps_per_token
- *   steps of the sequence; needs state.  All state-like buffers share one
+ *   intermediate [num_slots, int_tokens, HV, K, V] or NULL: snapshot i of
+ *   a slot is written once (i+1)*steps_per_token steps of the sequence are
+ *   done, i.e. when draft token i is complete; needs state.  All state-like buffers share one
  *   storage dtype (state_bf16).
  */
-int oracle_fused_recurrent_update(int B, int T, int H, int HV, int K, int V, const float* q,
-                                  const float* k, const float* v, const float* g,
-                                  const float* beta, int beta_per_v, float scale, int l2norm,
-                                  const int32_t* cu_seqlens, int N, int state_bf16, void* state,
-                                  int64_t num_slots, const int32_t* state_indices,
-                                  const void* initial_state, void* final_state,
-                                  void* intermediate, int64_t int_tokens, int steps_per_token,
-                                  float* o)
+typedef struct {
+    int T, H, HV, K, V;
+    const float* q;
+    const float* k;
+    const float* v;
+    const float* g;
+    const float* beta;
+    int beta_per_v;
+    float scale;
+    int l2norm;
+    const int32_t* cu_seqlens;
+    int state_bf16;
+    void* state;
+    int64_t num_slots;
+    const int32_t* state_indices;
+    const void* initial_state;
+    void* final_state;
+    void* intermediate;
+    int64_t int_tokens;
+    int steps_per_token;
+    float* o;
+} oracle_fused_args;
+
+/* One work item: sequence n, value head hv (item = n * HV + hv). */
+static int oracle_fused_item(const void* args, int64_t item)
+{
+    const oracle_fused_args* w = (const oracle_fused_args*)args;
+    const int H = w->H, HV = w->HV, K = w->K, V = w->V;
+    const int n = (int)(item / HV);
+    const int hv = (int)(item % HV);
+    const int G = HV / H;
+    const int64_t kv = (int64_t)K * V;
+    const float* q = w->q;
+    const float* k = w->k;
+    const float* v = w->v;
+    const float* g = w->g;
+    const float* beta = w->beta;
+    const int beta_per_v = w->beta_per_v;
+    void* state = w->state;
+    const int state_bf16 = w->state_bf16;
+    const void* initial_state = w->initial_state;
+    void* final_state = w->final_state;
+    void* intermediate = w->intermediate;
+    const int64_t int_tokens = w->int_tokens;
+    const int steps_per_token = w->steps_per_token;
+    float* o = w->o;
+
+    /* flat token range on the (B*T) axis */
+    int64_t f0, f1;
+    if (w->cu_seqlens) {
+        f0 = w->cu_seqlens[n];
+        f1 = w->cu_seqlens[n + 1];
+    } else {
+        f0 = (int64_t)n * w->T;
+        f1 = f0 + w->T;
+    }
+    int32_t idx = w->state_indices ? w->state_indices[n] : n;
+    const int h = hv / G;
+    if (state && w->state_indices && idx < 0) {
+        for (int64_t f = f0; f < f1; ++f)
+            for (int j = 0; j < V; ++j)
+                o[(f * HV + hv) * V + j] = 0.0f;
+        return 0;
+    }
+    if (state && (int64_t)idx >= w->num_slots)
+        return -2;
+
+    float* S = (float*)malloc(sizeof(float) * (size_t)kv);
+    float* qhat = (float*)malloc(sizeof(float) * (size_t)K);
+    float* khat = (float*)malloc(sizeof(float) * (size_t)K);
+    if (state)
+        oracle_load_block(state, state_bf16, ((int64_t)idx * HV + hv) * kv, kv, S);
+    else if (initial_state)
+        oracle_load_block(initial_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);
+    else
+        for (int64_t e = 0; e < kv; ++e)
+            S[e] = 0.0f;
+
+    for (int64_t f = f0; f < f1; ++f) {
+        const float* qt = q + (f * H + h) * K;
+        const float* kt = k + (f * H + h) * K;
+        if (w->l2norm) {
+            oracle_l2norm(K, qt, qhat);
+            oracle_l2norm(K, kt, khat);
+        } else {
+            for (int i = 0; i < K; ++i) {
+                qhat[i] = qt[i];
+                khat[i] = kt[i];
+            }
+        }
+        const float a = g ? expf(g[f * HV + hv]) : 1.0f;
+        float one = 1.0f;
+        const float* bt = &one;
+        int per_v = 0;
+        if (beta) {
+            bt = beta_per_v ? beta + (f * HV + hv) * V : beta + (f * HV + hv);
+            per_v = beta_per_v;
+        }
+        oracle_step(K, V, S, khat, qhat, v + (f * HV + hv) * V, a, bt, per_v, w->scale,
+                    o + (f * HV + hv) * V, NULL);
+        const int64_t step = f - f0 + 1;
+        if (intermediate && step % steps_per_token == 0) {
+            const int64_t i = step / steps_per_token - 1;
+            if (i < int_tokens)
+                oracle_store_block(intermediate, state_bf16,
+                                   (((int64_t)idx * int_tokens + i) * HV + hv) * kv, kv, S);
+        }
+    }
+    if (state)
+        oracle_store_block(state, state_bf16, ((int64_t)idx * HV + hv) * kv, kv, S);
+    else if (final_state)
+        oracle_store_block(final_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);
+    free(S);
+    free(qhat);
+    free(khat);
+    return 0;
+}
+
+int oracle_fused_recurrent_update_threads(int B, int T, int H, int HV, int K, int V,
+                                          const float* q, const float* k, const float* v,
+                                          const float* g, const float* beta, int beta_per_v,
+                                          float scale, int l2norm, const int32_t* cu_seqlens,
+                                          int N, int state_bf16, void* state, int64_t num_slots,
+                                          const int32_t* state_indices,
+                                          const void* initial_state, void* final_state,
+                                          void* intermediate, int64_t int_tokens,
+                                          int steps_per_token, float* o, int threads)
 {
     if (H <= 0 || HV % H != 0)
         return -1;
@@ -394,86 +644,27 @@ int oracle_fused_recurrent_update(int B, int T, int H, int HV, int K, int V, con
         N = B;
     if (intermediate && (!state || steps_per_token < 1))
         return -1;
-    const int G = HV / H;
-    const int64_t kv = (int64_t)K * V;
-    float* S = (float*)malloc(sizeof(float) * (size_t)kv);
-    float* qhat = (float*)malloc(sizeof(float) * (size_t)K);
-    float* khat = (float*)malloc(sizeof(float) * (size_t)K);
+    const oracle_fused_args w = {T, H, HV, K, V, q, k, v, g, beta, beta_per_v, scale, l2norm,
+                                 cu_seqlens, state_bf16, state, num_slots, state_indices,
+                                 initial_state, final_state, intermediate, int_tokens,
+                                 steps_per_token, o};
+    return oracle_farm(oracle_fused_item, &w, (int64_t)N * HV, threads);
+}
 
-    for (int n = 0; n < N; ++n) {
-        /* flat token range on the (B*T) axis */
-        int64_t f0, f1;
-        if (cu_seqlens) {
-            f0 = cu_seqlens[n];
-            f1 = cu_seqlens[n + 1];
-        } else {
-            f0 = (int64_t)n * T;
-            f1 = f0 + T;
-        }
-        int32_t idx = state_indices ? state_indices[n] : n;
-        for (int hv = 0; hv < HV; ++hv) {
-            const int h = hv / G;
-            if (state && state_indices && idx < 0) {
-                for (int64_t f = f0; f < f1; ++f)
-                    for (int j = 0; j < V; ++j)
-                        o[(f * HV + hv) * V + j] = 0.0f;
-                continue;
-            }
-            if (state && (int64_t)idx >= num_slots) {
-                free(S);
-                free(qhat);
-                free(khat);
-                return -2;
-            }
-            if (state)
-                oracle_load_block(state, state_bf16, ((int64_t)idx * HV + hv) * kv, kv, S);
-            else if (initial_state)
-                oracle_load_block(initial_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);
-            else
-                for (int64_t e = 0; e < kv; ++e)
-                    S[e] = 0.0f;
-
-            for (int64_t f = f0; f < f1; ++f) {
-                const float* qt = q + (f * H + h) * K;
-                const float* kt = k + (f * H + h) * K;
-                if (l2norm) {
-                    oracle_l2norm(K, qt, qhat);
-                    oracle_l2norm(K, kt, khat);
-                } else {
-                    for (int i = 0; i < K; ++i) {
-                        qhat[i] = qt[i];
-                        khat[i] = kt[i];
-                    }
-                }
-                const float a = g ? expf(g[f * HV + hv]) : 1.0f;
-                float one = 1.0f;
-                const float* bt = &one;
-                int per_v = 0;
-                if (beta) {
-                    bt = beta_per_v ? beta + (f * HV + hv) * V : beta + (f * HV + hv);
-                    per_v = beta_per_v;
-                }
-                oracle_step(K, V, S, khat, qhat, v + (f * HV + hv) * V, a, bt, per_v, scale,
-                            o + (f * HV + hv) * V, NULL);
-                const int64_t step = f - f0 + 1;
-                if (intermediate && step % steps_per_token == 0) {
-                    const int64_t i = step / steps_per_token - 1;
-                    if (i < int_tokens)
-                        oracle_store_block(intermediate, state_bf16,
-                                           (((int64_t)idx * int_tokens + i) * HV + hv) * kv, kv,
-                                           S);
-                }
-            }
-            if (state)
-                oracle_store_block(state, state_bf16, ((int64_t)idx * HV + hv) * kv, kv, S);
-            else if (final_state)
-                oracle_store_block(final_state, state_bf16, ((int64_t)n * HV + hv) * kv, kv, S);
-        }
-    }
-    free(S);
-    free(qhat);
-    free(khat);
-    return 0;
+int oracle_fused_recurrent_update(int B, int T, int H, int HV, int K, int V, const float* q,
+                                  const float* k, const float* v, const float* g,
+                                  const float* beta, int beta_per_v, float scale, int l2norm,
+                                  const int32_t* cu_seqlens, int N, int state_bf16, void* state,
+                                  int64_t num_slots, const int32_t* state_indices,
+                                  const void* initial_state, void* final_state,
+                                  void* intermediate, int64_t int_tokens, int steps_per_token,
+                                  float* o)
+{
+    return oracle_fused_recurrent_update_threads(B, T, H, HV, K, V, q, k, v, g, beta,
+                                                 beta_per_v, scale, l2norm, cu_seqlens, N,
+                                                 state_bf16, state, num_slots, state_indices,
+                                                 initial_state, final_state, intermediate,
+                                                 int_tokens, steps_per_token, o, 1);
 }
 
 /* [shape]: the forward's output is [total_seq_len, num_value_heads * V]. */
@@ -486,8 +677,9 @@ void oracle_fwd_output_shape(int64_t total_seq_len, int64_t nv, int64_t V, int64
 /* ------------------------------------------------- snapshot rollback ------ */
 
 /*
- * [gdp] intermediate_states: entry [slot, i] is the state after draft token i,
- * kept so that a verifier can return the recurrence to any accepted prefix.
+ * [gdp] update() parameters, intermediate_states: snapshot i of a slot holds
+ * the state once draft token i is complete; a verifier that accepts a prefix
+ * of the draft tokens restores the slot from the snapshot of the last one.
  * For request n with slot idx = state_indices[n] (>= 0) and accepted[n] = a
  * draft tokens, 1 <= a <= int_tokens: state[idx] <- intermediate[idx, a-1].
  * a == 0, a > int_tokens and padding requests (-1) leave the state alone (the

@@ -10,8 +10,18 @@ import gated_delta_rule_loop_amd as gdr
 from gated_delta_rule_loop_amd import workloads as wl
 
 REL_TOL = 2e-3          # max |got - ref| <= REL_TOL * max |ref|
-FLIP_MARGIN = 1e-4      # a bf16 flip is a tie only within this * max|ref| of the midpoint
+# A bf16 element that differs from the oracle's by a rounding flip is a tie
+# only if the oracle's unrounded float32 value lies within FLIP_MARGIN *
+# max|ref| of the midpoint between its two bf16 neighbours.  The GPU's float32
+# results differ from the oracle's by at most about 1e-6 of max|ref| (the
+# reduction order differs; measured on the full-size workloads and recorded
+# by test_float32_disagreement), so a genuine tie lies well inside 1e-5.
+FLIP_MARGIN = 1e-5
 FLIP_FRACTION = 1e-3    # at most this fraction of elements may be such ties
+
+# Running totals over the session, printed in pytest's terminal summary:
+# bf16 elements judged against the oracle and how many of them were ties.
+TIE_STATS = {"ties": 0, "elements": 0, "comparisons": 0, "max_tie_offset": 0.0}
 
 
 def dev(a):
@@ -138,6 +148,9 @@ def assert_state_close(got, ref, what, ref_unrounded=None, rel=REL_TOL):
     assert np.isfinite(g).all(), f"{what}: non-finite values"
     scale = max(np.abs(r).max(initial=0.0), 1e-30)
     bad = np.abs(g - r) > rel * scale
+    if got.dtype == np.uint16:
+        TIE_STATS["elements"] += int(got.size)
+        TIE_STATS["comparisons"] += 1
     if not bad.any():
         return 0
     assert got.dtype == np.uint16 and ref_unrounded is not None, (
@@ -153,7 +166,28 @@ def assert_state_close(got, ref, what, ref_unrounded=None, rel=REL_TOL):
                       f"rounding ties (max err {np.abs(g - r).max():.3e}, scale {scale:.3e})")
     n = int(bad.sum())
     assert n <= FLIP_FRACTION * got.size, f"{what}: {n} rounding ties (> {FLIP_FRACTION:.0e})"
+    TIE_STATS["ties"] += n
+    TIE_STATS["max_tie_offset"] = max(TIE_STATS["max_tie_offset"],
+                                      float((np.abs(u.astype(np.float64) - mid) / scale).max()))
     return n
+
+
+# Largest float32 gap between GPU and oracle states, relative to max|ref|, per
+# workload (reported in the terminal summary next to the ties).
+FP32_GAPS = {}
+
+
+def record_fp32_gap(what, got, ref):
+    """max |got - ref| / max |ref| of float32 states from the GPU and the
+    oracle; asserts it stays below a quarter of FLIP_MARGIN, the premise of
+    the tie rule, and records it."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape and np.isfinite(g).all(), what
+    gap = float(np.abs(g - r).max(initial=0.0) / max(np.abs(r).max(initial=0.0), 1e-30))
+    FP32_GAPS[what] = gap
+    assert gap <= FLIP_MARGIN / 4, f"{what}: float32 gap {gap:.2e} vs the oracle"
+    return gap
 
 
 def f32_pool(state):
