@@ -43,8 +43,8 @@ class GdrError(RuntimeError):
 _lib = None
 EXPORTS = ("gdr_recurrence_fwd", "gdr_recurrence_verify_ring", "gdr_state_fold",
            "gdr_fused_recurrent_update", "gdr_snapshot_rollback", "gdr_causal_conv1d",
-           "gdr_fwd_output_shape", "gdr_ring_record_elements", "gdr_last_error_message",
-           "gdr_version")
+           "gdr_fwd_output_shape", "gdr_check_indices", "gdr_set_debug_checks",
+           "gdr_ring_record_elements", "gdr_last_error_message", "gdr_version")
 
 
 def lib():
@@ -65,11 +65,14 @@ def lib():
         L.gdr_snapshot_rollback.argtypes = [P, P, P, P, vp]
         L.gdr_causal_conv1d.argtypes = [P, P, P, P, P, P, P, u32, vp]
         L.gdr_fwd_output_shape.argtypes = [P, P, ctypes.POINTER(ctypes.c_int64)]
+        i64 = ctypes.c_int64
+        L.gdr_check_indices.argtypes = [i64, vp, i64, vp, i64, vp, i64, i64, vp]
+        L.gdr_set_debug_checks.argtypes = [ctypes.c_int]
         L.gdr_ring_record_elements.argtypes = [i32, i32, i32]
         L.gdr_ring_record_elements.restype = ctypes.c_int64
         L.gdr_last_error_message.restype = ctypes.c_char_p
         L.gdr_version.restype = ctypes.c_char_p
-        for name in EXPORTS[:7]:
+        for name in EXPORTS[:9]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -218,6 +221,35 @@ def gdr_fwd_output_shape(qkv_conv_output, recurrent_state):
                                     _ref(describe(recurrent_state, allow_host=True)), out)
     _check("gdr_fwd_output_shape", rc)
     return (out[0], out[1])
+
+
+def gdr_check_indices(rows, *, row_offsets=None, total_tokens=0, slots=None, num_slots=0,
+                      ring_idx=None, ring_rows=0, ring_len=0, accepted=None):
+    """Host-side index check (host arrays: NumPy or CPU tensors of 32-bit
+    integers; -1 / 0xFFFFFFFF is padding).  Raises GdrError on a violation."""
+    import numpy as np  # noqa: PLC0415
+    keep = []
+
+    def ptr(a):
+        if a is None:
+            return None
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+        a = np.ascontiguousarray(a)
+        if a.dtype.itemsize != 4 or a.dtype.kind not in "iu":
+            raise TypeError("index arrays must hold 32-bit integers")
+        keep.append(a)
+        return a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = lib().gdr_check_indices(int(rows), ptr(row_offsets), int(total_tokens), ptr(slots),
+                                 int(num_slots), ptr(ring_idx), int(ring_rows), int(ring_len),
+                                 ptr(accepted))
+    _check("gdr_check_indices", rc)
+
+
+def gdr_set_debug_checks(enable):
+    """Turn the per-call index checks on or off; returns the previous setting."""
+    return bool(lib().gdr_set_debug_checks(1 if enable else 0))
 
 
 def gdr_ring_record_elements(group, key_head_dim, value_head_dim):

@@ -1,12 +1,18 @@
 // Host side of the C ABI declared in include/gdr.h: argument validation,
 // launch-shape choice and dispatch to the gfx950 kernels.  Nothing here
-// allocates, frees or synchronises device memory.
+// allocates, frees or synchronises device memory, except the optional index
+// checks (gdr_set_debug_checks), which copy index vectors to the host.
 #include "gdr.h"
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "gdr_internal.h"
 
@@ -138,6 +144,123 @@ int check_state(const char* fn, const char* name, const gdr_tensor* t, int ndim,
     return check_layout(fn, name, t, t->dtype == GDR_DTYPE_BF16 ? 8 : 4);
 }
 
+// ------------------------------------------------------- index checks ---
+
+// Index contents are preconditions; these checks run only when asked for
+// (gdr_check_indices on host arrays, or every call once gdr_set_debug_checks
+// is on).  -1: not decided yet (the environment decides on first use).
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks_on() {
+    int v = g_debug_checks.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = std::getenv("GDR_DEBUG_CHECK_SLOTS");
+        int want = (e != nullptr && std::strtol(e, nullptr, 10) != 0) ? 1 : 0;
+        g_debug_checks.compare_exchange_strong(v, want);
+        v = g_debug_checks.load(std::memory_order_relaxed);
+    }
+    return v > 0;
+}
+
+// Values of `idx` at the rows where `use` holds must be below `limit` and
+// pairwise distinct.
+template <typename Use>
+int check_distinct_below(const char* fn, const char* what, int64_t rows, const uint32_t* idx,
+                         int64_t limit, const char* limit_name, Use use) {
+    std::vector<std::pair<uint32_t, int64_t>> seen;
+    seen.reserve(static_cast<size_t>(rows));
+    for (int64_t b = 0; b < rows; ++b) {
+        if (!use(b)) continue;
+        if (static_cast<int64_t>(idx[b]) >= limit)
+            return fail(GDR_ERR_INVALID_ARG, "%s: %s %u of row %lld is not below the %lld %s", fn,
+                        what, idx[b], static_cast<long long>(b), static_cast<long long>(limit),
+                        limit_name);
+        seen.emplace_back(idx[b], b);
+    }
+    std::sort(seen.begin(), seen.end());
+    for (size_t i = 1; i < seen.size(); ++i)
+        if (seen[i].first == seen[i - 1].first)
+            return fail(GDR_ERR_INVALID_ARG, "%s: %s %u is used by rows %lld and %lld (two rows "
+                        "on one %s race)", fn, what, seen[i].first,
+                        static_cast<long long>(seen[i - 1].second),
+                        static_cast<long long>(seen[i].second), what);
+    return GDR_OK;
+}
+
+int check_indices_impl(const char* fn, int64_t rows, const uint32_t* off, int64_t total_tokens,
+                       const uint32_t* slots, int64_t num_slots, const uint32_t* ring_idx,
+                       int64_t ring_rows, int64_t ring_len, const uint32_t* accepted) {
+    if (rows < 0) return fail(GDR_ERR_INVALID_ARG, "%s: negative row count", fn);
+    if (off) {
+        for (int64_t b = 0; b < rows; ++b)
+            if (off[b + 1] < off[b])
+                return fail(GDR_ERR_INVALID_ARG, "%s: row offsets decrease at row %lld (%u, then "
+                            "%u)", fn, static_cast<long long>(b), off[b], off[b + 1]);
+        if (static_cast<int64_t>(off[rows]) > total_tokens)
+            return fail(GDR_ERR_INVALID_ARG, "%s: row offsets end at %u, past the %lld tokens", fn,
+                        off[rows], static_cast<long long>(total_tokens));
+    }
+    auto active = [&](int64_t b) { return slots == nullptr || slots[b] != gdr::kPadSlot; };
+    int rc;
+    if (slots && (rc = check_distinct_below(fn, "slot", rows, slots, num_slots, "pool slots",
+                                            active)))
+        return rc;
+    if (ring_idx && (accepted || off)) {
+        auto uses_ring = [&](int64_t b) {
+            if (!active(b)) return false;
+            const int64_t n = accepted ? static_cast<int64_t>(accepted[b])
+                                       : static_cast<int64_t>(off[b + 1]) - off[b];
+            return n > 0 && n <= ring_len;
+        };
+        if ((rc = check_distinct_below(fn, "ring row", rows, ring_idx, ring_rows, "ring rows",
+                                       uses_ring)))
+            return rc;
+    }
+    return GDR_OK;
+}
+
+// Copies n index elements (u32 or i32 bits) of t to the host; synchronises
+// the stream.  Debug checks only.
+int fetch_indices(const char* fn, const char* name, const gdr_tensor* t, int64_t n,
+                  hipStream_t stream, std::vector<uint32_t>& out) {
+    out.assign(static_cast<size_t>(n), 0u);
+    if (n == 0) return GDR_OK;
+    hipError_t e = hipMemcpyAsync(out.data(), t->data, static_cast<size_t>(n) * sizeof(uint32_t),
+                                  hipMemcpyDefault, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail(GDR_ERR_HIP, "%s: index check could not read %s: %s", fn, name,
+                    hipGetErrorString(e));
+    return GDR_OK;
+}
+
+// The checks of one call, on its device index vectors (nullptr: absent).
+struct IndexCheck {
+    const gdr_tensor* offsets = nullptr;
+    int64_t total_tokens = 0;
+    const gdr_tensor* slots = nullptr;
+    int64_t num_slots = 0;
+    const gdr_tensor* ring_idx = nullptr;
+    int64_t ring_rows = 0, ring_len = 0;
+    const gdr_tensor* accepted = nullptr;
+};
+
+int run_debug_check(const char* fn, int64_t rows, const IndexCheck& c, void* stream) {
+    if (!debug_checks_on()) return GDR_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<uint32_t> off, sl, ring, acc;
+    int rc;
+    if ((c.offsets && (rc = fetch_indices(fn, "row offsets", c.offsets, rows + 1, s, off))) ||
+        (c.slots && (rc = fetch_indices(fn, "slots", c.slots, rows, s, sl))) ||
+        (c.ring_idx && (rc = fetch_indices(fn, "ring rows", c.ring_idx, rows, s, ring))) ||
+        (c.accepted && (rc = fetch_indices(fn, "accepted counts", c.accepted, rows, s, acc))))
+        return rc;
+    return check_indices_impl(fn, rows, c.offsets ? off.data() : nullptr, c.total_tokens,
+                              c.slots ? sl.data() : nullptr, c.num_slots,
+                              c.ring_idx ? ring.data() : nullptr, c.ring_rows, c.ring_len,
+                              c.accepted ? acc.data() : nullptr);
+}
+
 float resolve_scale(float scale, int64_t K) {
     if (!(scale > 0.0f)) return 1.0f / std::sqrt(static_cast<float>(K));
     return scale;
@@ -172,9 +295,9 @@ gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t to
     const bool long_rows = rows > 0 && total_tokens >= 16 * rows;
     const bool decode = rows > 0 && 2 * total_tokens <= 3 * rows;  // ~1 token per row
     if (K == 128 && K != V && e == Entry::Fused && !long_rows) {
-        s.cpl = GDR_FUSED_CPL;  // as the K == V == 128 fused profile
-        s.chunk = GDR_FUSED_CHUNK;
-        s.kg_low = GDR_FUSED_KGLOW;
+        s.cpl = gdr::kFusedCpl;  // as the K == V == 128 fused profile
+        s.chunk = gdr::kFusedChunk;
+        s.kg_low = gdr::kFusedKgLow;
     } else if (K == 256 || K != V) {  // one short and one long-row shape per pair
         if (e == Entry::Fold || !long_rows) {
             s.cpl = K == 256 ? 2 : (K == 64 ? 8 : 4);
@@ -186,28 +309,28 @@ gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t to
         }
     } else if (K == 128) {
         if (e == Entry::Fold) {
-            s.cpl = GDR_FOLD_CPL;
+            s.cpl = gdr::kFoldCpl;
             s.chunk = 1;
         } else if (long_rows) {
-            s.cpl = GDR_LONG_CPL;
-            s.chunk = GDR_LONG_CHUNK;
-            s.kg_low = GDR_LONG_KGLOW;
+            s.cpl = gdr::kLongCpl;
+            s.chunk = gdr::kLongChunk;
+            s.kg_low = gdr::kLongKgLow;
         } else if (e == Entry::Fused && !decode) {
-            s.cpl = GDR_FUSED_CPL;
-            s.chunk = GDR_FUSED_CHUNK;
-            s.kg_low = GDR_FUSED_KGLOW;
+            s.cpl = gdr::kFusedCpl;
+            s.chunk = gdr::kFusedChunk;
+            s.kg_low = gdr::kFusedKgLow;
         } else if (decode) {
             // A batch whose decode shape would give 256 waves or fewer (4 rows
             // at 32 value heads) is latency-bound: narrower tiles spread it
             // over 4x the waves.
-            const bool tiny = rows * nv * (V / (gdr::kLanesPerRow * GDR_DECODE_CPL)) <= 256;
-            s.cpl = tiny ? GDR_TINY_CPL : GDR_DECODE_CPL;
-            s.chunk = GDR_DECODE_CHUNK;
-            s.kg_low = GDR_DECODE_KGLOW;
+            const bool tiny = rows * nv * (V / (gdr::kLanesPerRow * gdr::kDecodeCpl)) <= 256;
+            s.cpl = tiny ? gdr::kTinyCpl : gdr::kDecodeCpl;
+            s.chunk = gdr::kDecodeChunk;
+            s.kg_low = gdr::kDecodeKgLow;
         } else {
-            s.cpl = GDR_SHORT_CPL;
-            s.chunk = GDR_SHORT_CHUNK;
-            s.kg_low = GDR_SHORT_KGLOW;
+            s.cpl = gdr::kShortCpl;
+            s.chunk = gdr::kShortChunk;
+            s.kg_low = gdr::kShortKgLow;
         }
     } else if (long_rows && e != Entry::Fold) {
         s.cpl = 2;
@@ -349,6 +472,17 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     p.scale = resolve_scale(scale, K);
     p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
     p.order = order_rows(s, p);
+    IndexCheck ic;
+    ic.offsets = offsets;
+    ic.total_tokens = T;
+    ic.slots = slot_idx;
+    ic.num_slots = state->shape[0];
+    if (ring) {
+        ic.ring_idx = ring_slot_idx;
+        ic.ring_rows = ring->shape[0];
+        ic.ring_len = ring->shape[2];
+    }
+    if ((rc = run_debug_check(fn, B, ic, stream))) return rc;
     const gdr::StateType st =
         state->dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
     return hip_status(fn, gdr::launch_recurrence(p, s, st, work == GDR_DTYPE_BF16,
@@ -441,6 +575,14 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
     p.ring_tok = ring->stride[2];
     p.ring_len = static_cast<int32_t>(ring->shape[2]);
     p.accepted = as_u32(accepted);
+    IndexCheck ic;
+    ic.slots = slot_idx;
+    ic.num_slots = recurrent_state->shape[0];
+    ic.ring_idx = ring_slot_idx;
+    ic.ring_rows = ring->shape[0];
+    ic.ring_len = ring->shape[2];
+    ic.accepted = accepted;
+    if ((rc = run_debug_check(fn, B, ic, stream))) return rc;
     const gdr::StateType st =
         recurrent_state->dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
     return hip_status(fn, gdr::launch_fold(p, s, st, static_cast<hipStream_t>(stream)));
@@ -598,6 +740,16 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     p.scale = resolve_scale(scale, K);
     p.l2norm = (flags & GDR_FLAG_L2NORM_QK) ? 1 : 0;
     p.order = order_rows(s, p);
+    IndexCheck ic;
+    if (present(cu_seqlens)) {
+        ic.offsets = cu_seqlens;
+        ic.total_tokens = T;
+    }
+    if (present(state) && present(state_indices)) {
+        ic.slots = state_indices;
+        ic.num_slots = state->shape[0];
+    }
+    if ((rc = run_debug_check(fn, N, ic, stream))) return rc;
     const gdr::StateType st =
         st_dtype == GDR_DTYPE_BF16 ? gdr::StateType::BF16 : gdr::StateType::F32;
     return hip_status(fn, gdr::launch_recurrence(p, s, st, work == GDR_DTYPE_BF16,
@@ -645,6 +797,10 @@ int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indic
     p.in_head = intermediate_states->stride[2] * es;
     p.int_tokens = static_cast<int32_t>(intermediate_states->shape[1]);
     p.block16 = block16;
+    IndexCheck ic;
+    ic.slots = state_indices;
+    ic.num_slots = S;
+    if ((rc = run_debug_check(fn, N, ic, stream))) return rc;
     return hip_status(fn, gdr::launch_rollback(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -719,6 +875,14 @@ int gdr_causal_conv1d(const gdr_tensor* out, const gdr_tensor* x, const gdr_tens
     p.weight = static_cast<const float*>(weight->data);
     p.w_chan = weight->stride[0];
     p.bias = present(bias) ? static_cast<const float*>(bias->data) : nullptr;
+    IndexCheck ic;
+    ic.offsets = input_row_offsets;
+    ic.total_tokens = T;
+    if (present(conv_state) && present(slot_idx)) {
+        ic.slots = slot_idx;
+        ic.num_slots = conv_state->shape[0];
+    }
+    if ((rc = run_debug_check(fn, B, ic, stream))) return rc;
     return hip_status(fn, gdr::launch_conv(p, work == GDR_DTYPE_BF16,
                                            static_cast<hipStream_t>(stream)));
 }
@@ -740,6 +904,21 @@ int64_t gdr_ring_record_elements(int32_t group, int32_t key_head_dim, int32_t va
     if (group < 1 || key_head_dim < 1 || value_head_dim < 1) return -1;
     return static_cast<int64_t>(key_head_dim) +
            static_cast<int64_t>(group) * (static_cast<int64_t>(value_head_dim) + 1);
+}
+
+int gdr_check_indices(int64_t rows, const uint32_t* row_offsets, int64_t total_tokens,
+                      const uint32_t* slots, int64_t num_slots, const uint32_t* ring_idx,
+                      int64_t ring_rows, int64_t ring_len, const uint32_t* accepted) {
+    const int rc = check_indices_impl("gdr_check_indices", rows, row_offsets, total_tokens, slots,
+                                      num_slots, ring_idx, ring_rows, ring_len, accepted);
+    if (rc == GDR_OK) g_last_error.clear();
+    return rc;
+}
+
+int gdr_set_debug_checks(int enable) {
+    const int before = debug_checks_on() ? 1 : 0;
+    g_debug_checks.store(enable ? 1 : 0, std::memory_order_relaxed);
+    return before;
 }
 
 const char* gdr_last_error_message(void) { return g_last_error.c_str(); }

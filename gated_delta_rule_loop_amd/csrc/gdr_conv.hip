@@ -50,7 +50,9 @@ __device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
     *reinterpret_cast<uint2*>(p) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
 }
 
-// Row of token t: the last b in [0, B) with offsets[b] <= t (t < offsets[B]).
+// Row of token t: the last b in [0, B) with offsets[b] <= t.  Callers use it
+// for offsets[0] <= t < offsets[B] only (and for a run start outside that
+// range, whose tokens are then skipped).
 __device__ __forceinline__ int row_of(const uint32_t* off, int B, uint32_t t) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
@@ -84,13 +86,18 @@ __global__ void __launch_bounds__(kConvThreads) conv_out_kernel(const ConvParams
 
     int b = row_of(p.offsets, p.B, static_cast<uint32_t>(tstart));
     int t0 = static_cast<int>(p.offsets[b]), t1 = static_cast<int>(p.offsets[b + 1]);
+    // Tokens outside [offsets[0], offsets[B]) belong to no row: nothing is
+    // read or written for them (x may be a padded token buffer).
+    const int t_first = static_cast<int>(p.offsets[0]);
+    const int t_end = min(p.T, static_cast<int>(p.offsets[p.B]));
     float win[H][kConvVec];  // win[i]: input at position t - H + i
     bool fresh = true;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int t = tstart + i;
-        if (t >= p.T) break;
-        while (t >= t1) {  // next non-empty row
+        if (t >= t_end) break;
+        if (t < t_first) continue;
+        while (t >= t1) {  // next non-empty row (t < offsets[B], so b stays below B)
             ++b;
             t0 = t1;
             t1 = static_cast<int>(p.offsets[b + 1]);

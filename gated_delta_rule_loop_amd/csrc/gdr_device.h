@@ -236,9 +236,6 @@ struct RawCols<uint16_t, CPL> {
 // which rely on the cache to merge the halves, so they stay ordinary
 // (measured: non-temporal 8-byte state accesses slowed the decode step by 20%,
 // 16-byte ones sped the snapshot-heavy fused update up by 9%).
-#ifndef GDR_NT_STATE
-#define GDR_NT_STATE 1
-#endif
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -246,12 +243,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool NT, typename T>
 __device__ __forceinline__ T state_ld(const T* p) {
-    if constexpr (NT && GDR_NT_STATE) return __builtin_nontemporal_load(p);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
     return *p;
 }
 template <bool NT, typename T>
 __device__ __forceinline__ void state_st(T v, T* p) {
-    if constexpr (NT && GDR_NT_STATE) __builtin_nontemporal_store(v, p);
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
 
@@ -1052,12 +1049,11 @@ hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_
 #define GDR_REC_CASE(KK, VV, CC, CH, KL)                                              \
     if (s.K == KK && s.V == VV && s.cpl == CC && s.chunk == CH && s.kg_low == KL)    \
         return launch_rec_mode<KK, VV, CC, CH, ST, KL, WT, MODE>(p, s.wpg, stream);
-    GDR_REC_CASE(128, 128, GDR_DECODE_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
-    GDR_REC_CASE(128, 128, GDR_TINY_CPL, GDR_DECODE_CHUNK, GDR_DECODE_KGLOW)
-    GDR_REC_CASE(128, 128, GDR_SHORT_CPL, GDR_SHORT_CHUNK, GDR_SHORT_KGLOW)
-    GDR_REC_CASE(128, 128, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
-    GDR_REC_CASE(128, 128, GDR_LONG_CPL, GDR_LONG_CHUNK, GDR_LONG_KGLOW)
-#ifndef GDR_ONLY_K128
+    GDR_REC_CASE(128, 128, kDecodeCpl, kDecodeChunk, kDecodeKgLow)
+    GDR_REC_CASE(128, 128, kTinyCpl, kDecodeChunk, kDecodeKgLow)
+    GDR_REC_CASE(128, 128, kShortCpl, kShortChunk, kShortKgLow)
+    GDR_REC_CASE(128, 128, kFusedCpl, kFusedChunk, kFusedKgLow)
+    GDR_REC_CASE(128, 128, kLongCpl, kLongChunk, kLongKgLow)
     GDR_REC_CASE(256, 256, 2, 8, false)
     GDR_REC_CASE(256, 256, 1, 8, true)
     GDR_REC_CASE(64, 64, 8, 8, false)
@@ -1070,13 +1066,12 @@ hipError_t launch_rec_table(const RecParams& p, const LaunchShape& s, hipStream_
         GDR_REC_CASE(64, 128, 8, 8, false)
         GDR_REC_CASE(64, 128, 2, 16, true)
         GDR_REC_CASE(128, 64, 1, 16, true)
-        GDR_REC_CASE(128, 256, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
-        GDR_REC_CASE(128, 64, GDR_FUSED_CPL, GDR_FUSED_CHUNK, GDR_FUSED_KGLOW)
+        GDR_REC_CASE(128, 256, kFusedCpl, kFusedChunk, kFusedKgLow)
+        GDR_REC_CASE(128, 64, kFusedCpl, kFusedChunk, kFusedKgLow)
         GDR_REC_CASE(128, 256, 1, 16, true)
         GDR_REC_CASE(256, 128, 2, 8, false)
         GDR_REC_CASE(256, 128, 1, 8, true)
     }
-#endif
 #undef GDR_REC_CASE
     return hipErrorInvalidValue;
 }

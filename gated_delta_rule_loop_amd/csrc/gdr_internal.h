@@ -106,52 +106,26 @@ hipError_t launch_conv(const ConvParams& p, bool work_bf16, hipStream_t stream);
 constexpr int kRollbackThreads = 256;
 constexpr int kRollbackPerThread = 8;  // 16-byte vectors per thread
 
-// Launch profiles at K = 128 (value columns per lane, tokens per stage).  The
-// reduction order does not depend on them, so they are free tuning choices:
-// decode (about one token per row), short windows (verify), the fused update
-// on short rows (GDP decode, snapshot-heavy), and long rows (prefill).
-#ifndef GDR_DECODE_CPL
-#define GDR_DECODE_CPL 8
-#endif
-#ifndef GDR_TINY_CPL
-#define GDR_TINY_CPL 2  // decode batches of at most 256 waves at GDR_DECODE_CPL
-#endif
-#ifndef GDR_DECODE_CHUNK
-#define GDR_DECODE_CHUNK 1
-#endif
-#ifndef GDR_SHORT_CPL
-#define GDR_SHORT_CPL 4
-#endif
-#ifndef GDR_SHORT_CHUNK
-#define GDR_SHORT_CHUNK 8
-#endif
-#ifndef GDR_FUSED_CPL
-#define GDR_FUSED_CPL 8
-#endif
-#ifndef GDR_FUSED_CHUNK
-#define GDR_FUSED_CHUNK 4
-#endif
-#ifndef GDR_LONG_CPL
-#define GDR_LONG_CPL 1
-#endif
-#ifndef GDR_LONG_CHUNK
-#define GDR_LONG_CHUNK 32
-#endif
-#ifndef GDR_DECODE_KGLOW
-#define GDR_DECODE_KGLOW false
-#endif
-#ifndef GDR_SHORT_KGLOW
-#define GDR_SHORT_KGLOW false
-#endif
-#ifndef GDR_FUSED_KGLOW
-#define GDR_FUSED_KGLOW false
-#endif
-#ifndef GDR_LONG_KGLOW
-#define GDR_LONG_KGLOW true
-#endif
-#ifndef GDR_FOLD_CPL
-#define GDR_FOLD_CPL 4
-#endif
+// Launch profiles at K = 128 (value columns per lane, tokens per stage, lane
+// layout).  The reduction order does not depend on them, so they are free
+// tuning choices: decode (about one token per row), tiny decode batches (at
+// most 256 waves at the decode tiling), short windows (verify), the fused
+// update on short rows (GDP decode, snapshot-heavy), long rows (prefill) and
+// the fold.
+constexpr int kDecodeCpl = 8;
+constexpr int kTinyCpl = 2;
+constexpr int kDecodeChunk = 1;
+constexpr bool kDecodeKgLow = false;
+constexpr int kShortCpl = 4;
+constexpr int kShortChunk = 8;
+constexpr bool kShortKgLow = false;
+constexpr int kFusedCpl = 8;
+constexpr int kFusedChunk = 4;
+constexpr bool kFusedKgLow = false;
+constexpr int kLongCpl = 1;
+constexpr int kLongChunk = 32;
+constexpr bool kLongKgLow = true;
+constexpr int kFoldCpl = 4;
 
 // Columns per wave for a given lanes-per-column setting.
 constexpr int kLanesPerRow = 8;   // lanes that share one key-row group

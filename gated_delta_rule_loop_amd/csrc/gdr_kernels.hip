@@ -230,13 +230,11 @@ static hipError_t launch_fold_wpg(const FoldParams& p, int wpg, hipStream_t stre
 template <typename ST>
 static hipError_t launch_fold_st(const FoldParams& p, const LaunchShape& s, hipStream_t stream) {
     switch (s.K) {
-        case 128: return s.cpl == GDR_FOLD_CPL ? launch_fold_wpg<128, GDR_FOLD_CPL, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
-#ifndef GDR_ONLY_K128
+        case 128: return s.cpl == kFoldCpl ? launch_fold_wpg<128, kFoldCpl, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 256: return s.cpl == 2 ? launch_fold_wpg<256, 2, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 64: return s.cpl == 8 ? launch_fold_wpg<64, 8, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 32: return s.cpl == 4 ? launch_fold_wpg<32, 4, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 16: return s.cpl == 2 ? launch_fold_wpg<16, 2, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
-#endif
         default: return hipErrorInvalidValue;
     }
 }

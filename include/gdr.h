@@ -35,8 +35,10 @@
  *     checks happen on the host before anything is enqueued; a failed check
  *     enqueues nothing.
  *   - Index contents (offsets, slots) are preconditions and are not checked
- *     on the device: offsets non-decreasing, slots below the pool size and
- *     distinct within one call (two rows on one slot race).  Slot
+ *     on the device: offsets non-decreasing and ending at or before the
+ *     token count, slots below the pool size and distinct within one call
+ *     (two rows on one slot race).  gdr_check_indices checks them on the
+ *     host, and gdr_set_debug_checks makes every call check its own.  Slot
  *     0xFFFFFFFF (-1 as int32) marks a padding row in every entry point: its
  *     output rows are written as +0.0 and no state, ring or snapshot memory
  *     is read or written for it.
@@ -108,7 +110,9 @@ typedef struct gdr_tensor {
  *                     2*nk*K + hv*V + ...
  *   decay_per_token   [T, nv] work    multiplicative decay a_t
  *   beta_per_token    [T, nv] work    beta gate
- *   input_row_offsets [B+1] u32|i32   row b spans [off[b], off[b+1])
+ *   input_row_offsets [B+1] u32|i32   row b spans [off[b], off[b+1]); tokens
+ *                     outside [off[0], off[B]) belong to no row and their
+ *                     output rows are not written
  *   scale             <= 0 or NaN selects 1/sqrt(K)
  *   flags             GDR_FLAG_L2NORM_QK (the page always normalises; pass it)
  */
@@ -258,7 +262,9 @@ int gdr_snapshot_rollback(const gdr_tensor* state, const gdr_tensor* state_indic
  *                     the last W-1 inputs of history ++ row
  *   slot_idx          [B] u32|i32 conv_state slot per row (absent: slot = row);
  *                     0xFFFFFFFF = padding (zero output, nothing touched)
- *   input_row_offsets [B+1] u32|i32 (B is shape[0] - 1)
+ *   input_row_offsets [B+1] u32|i32 (B is shape[0] - 1); tokens of x
+ *                     outside [off[0], off[B]) belong to no row: they are not
+ *                     read and their output rows are not written
  *   flags             GDR_FLAG_CONV_SILU or 0
  * Rows of length 0 touch nothing.  Two kernel launches on `stream` (outputs,
  * then the history update).
@@ -284,6 +290,41 @@ int gdr_fwd_output_shape(const gdr_tensor* qkv_conv_output, const gdr_tensor* re
  * ring_record_stride).  Returns -1 for non-positive arguments.
  */
 int64_t gdr_ring_record_elements(int32_t group, int32_t key_head_dim, int32_t value_head_dim);
+
+/*
+ * gdr_check_indices - host-side check of the index contents that every entry
+ * point takes as preconditions (the kernels do not check them).  The arrays
+ * are HOST memory; NULL skips that part of the check.
+ *   rows          number of batch rows (or requests)
+ *   row_offsets   [rows+1]: must not decrease, and must end at or before
+ *                 total_tokens (input_row_offsets, or cu_seqlens as u32 bits)
+ *   slots         [rows]: 0xFFFFFFFF (-1 as int32) is padding; any other
+ *                 value must be below num_slots and used by one row only
+ *   ring_idx      [rows] ring row of each row, checked for the rows that
+ *                 use the ring: non-padding rows that record in a verify
+ *                 (length <= ring_len; needs row_offsets) or, when accepted
+ *                 is given, rows that a fold applies (0 < accepted <= ring_len).
+ *                 Those must be below ring_rows and pairwise distinct.
+ *   accepted      [rows] fold counts, or NULL for a verify
+ * Returns GDR_OK, or GDR_ERR_INVALID_ARG with a message naming the first
+ * offending row.  Host only; enqueues nothing.
+ */
+int gdr_check_indices(int64_t rows, const uint32_t* row_offsets, int64_t total_tokens,
+                      const uint32_t* slots, int64_t num_slots, const uint32_t* ring_idx,
+                      int64_t ring_rows, int64_t ring_len, const uint32_t* accepted);
+
+/*
+ * gdr_set_debug_checks - turn the index checks on (enable != 0) or off for
+ * every later call in the process; returns the previous setting.  The
+ * initial setting is on when the environment variable GDR_DEBUG_CHECK_SLOTS
+ * holds a non-zero number.  With the checks on, each entry point copies its
+ * index vectors to the host (this synchronises the caller's stream, so
+ * checked calls cannot be captured into a HIP graph) and runs
+ * gdr_check_indices on them before enqueueing anything; a failed check
+ * returns GDR_ERR_INVALID_ARG and enqueues nothing.  A debugging aid for
+ * callers that suspect duplicate or out-of-range slots; off by default.
+ */
+int gdr_set_debug_checks(int enable);
 
 /* Message of the last failed call on this thread ("" when none). */
 const char* gdr_last_error_message(void);

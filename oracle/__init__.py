@@ -20,7 +20,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libgdr_oracle.so")
+# GDR_ORACLE_LIB selects another build of gdr_oracle.c (the sanitizer build
+# of oracle/build.py --sanitize); the default is the plain build.
+_LIB_PATH = os.environ.get("GDR_ORACLE_LIB") or os.path.join(_HERE, "libgdr_oracle.so")
 _lib = None
 
 PAD_SLOT = 0xFFFFFFFF

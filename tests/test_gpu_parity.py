@@ -7,7 +7,9 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
+import gated_delta_rule_loop_amd as gdr
 import oracle
 from gated_delta_rule_loop_amd import workloads as wl
 from tests import gpu_harness as H
@@ -759,6 +761,98 @@ def test_conv_one_token_rows(W):
     H.assert_close(out_g, out_r, f"conv mixed rows W={W}")
     assert np.array_equal(st_g, st_r), "mixed rows history"
     say(f"conv one-token rows W={W}: ok")
+
+
+@pytest.mark.parametrize("shape", ["runs", "one_token"])
+def test_conv_tokens_outside_rows(shape):
+    """x holds tokens before offsets[0] and after offsets[B] (a padded token
+    buffer): they belong to no row, so their output rows keep their previous
+    contents and nothing is read for them; the rows themselves match the
+    oracle, histories bit for bit.  Both launch shapes (8-token runs, and one
+    token per thread when rows average under four tokens)."""
+    rng = np.random.Generator(np.random.PCG64(131 if shape == "runs" else 132))
+    if shape == "runs":
+        lengths, lead, trail = [7, 0, 15, 3], 3, 21
+    else:
+        lengths, lead, trail = [1] * 10 + [2], 2, 9
+    m = wl.conv_inputs(rng, lengths, C=128, W=4, slots=16)
+    T_rows = m["x"].shape[0]
+    x = rng.standard_normal((lead + T_rows + trail, 128)).astype(np.float32)
+    x[lead:lead + T_rows] = m["x"]
+    off = (m["row_offsets"].astype(np.int64) + lead).astype(np.uint32)
+    T = x.shape[0]
+    B = len(lengths)
+    assert (T >= 4 * B) == (shape == "runs")
+    xs = H.dev(x)
+    out = torch.full((T, 128), float("nan"), device="cuda")
+    st = H.dev(m["conv_state"])
+    gdr.gdr_causal_conv1d(xs, H.dev(m["weight"]), H.dev(off), bias=H.dev(m["bias"]),
+                          conv_state=st, slot_idx=H.dev(m["slot_idx"]), silu=True, out=out)
+    torch.cuda.synchronize()
+    out_g, st_g = H.host(out), H.host(st)
+    out_r, st_r = oracle.causal_conv1d(x=x, weight=m["weight"], slot_idx=m["slot_idx"],
+                                       row_offsets=off, bias=m["bias"],
+                                       conv_state=m["conv_state"], silu=True)
+    rows = slice(int(off[0]), int(off[-1]))
+    H.assert_close(out_g[rows], out_r[rows], f"conv rows between padding tokens ({shape})")
+    assert np.isnan(out_g[:int(off[0])]).all() and np.isnan(out_g[int(off[-1]):]).all(), (
+        "tokens outside the rows were written")
+    assert np.array_equal(st_g, st_r), "history"
+    say(f"conv with {lead} leading and {trail} trailing tokens ({shape}): ok")
+
+
+def test_debug_index_checks():
+    """With gdr_set_debug_checks on, every entry point checks its device index
+    vectors before enqueueing: a repeated slot, an offset past the tokens or a
+    ring row out of range is rejected with nothing written, and valid calls
+    give the same bits as with the checks off."""
+    w = wl.verify_window()
+    before = gdr.gdr_set_debug_checks(True)
+    try:
+        out_on, st_on, ring_on = H.gpu_verify(w)
+        fold_on = H.gpu_fold(w, st_on, ring_on, w["accepted"])
+        fo, fs = H.gpu_fwd(w)
+        g = wl.gdp_decode()
+        o_on, s_on, i_on = H.gpu_fused(g)
+        bad = dict(w, slot_idx=w["slot_idx"].copy())
+        bad["slot_idx"][5] = bad["slot_idx"][9]
+        with pytest.raises(gdr.GdrError, match="used by rows 5 and 9"):
+            H.gpu_fwd(bad)
+        past = dict(w, row_offsets=w["row_offsets"].copy())
+        past["row_offsets"][-1] += 1
+        with pytest.raises(gdr.GdrError, match="past the"):
+            H.gpu_fwd(past)
+        lens = np.diff(w["row_offsets"].astype(np.int64))
+        rec = int(np.flatnonzero(lens <= w["ring"].shape[2])[0])
+        ring_bad = dict(w, ring_slot_idx=w["ring_slot_idx"].copy())
+        ring_bad["ring_slot_idx"][rec] = w["ring"].shape[0]
+        with pytest.raises(gdr.GdrError, match=f"ring row {w['ring'].shape[0]} of row {rec}"):
+            H.gpu_verify(ring_bad)
+        gbad = dict(g, state_indices=g["state_indices"].copy())
+        act = np.flatnonzero(gbad["state_indices"] >= 0)
+        gbad["state_indices"][act[1]] = gbad["state_indices"][act[0]]
+        with pytest.raises(gdr.GdrError, match="used by rows"):
+            H.gpu_fused(gbad)
+        # a rejected call wrote nothing
+        st_t = H.dev(w["state"])
+        out_t = torch.full((w["qkv"].shape[0], 32 * 128), float("nan"), device="cuda")
+        with pytest.raises(gdr.GdrError):
+            gdr.gdr_recurrence_fwd(out_t, st_t, H.dev(bad["slot_idx"]), H.dev(w["qkv"]),
+                                   H.dev(w["decay"]), H.dev(w["beta"]), H.dev(w["row_offsets"]),
+                                   num_value_heads=32, num_key_heads=16)
+        torch.cuda.synchronize()
+        assert np.array_equal(H.host(st_t), w["state"]) and torch.isnan(out_t).all().item()
+    finally:
+        gdr.gdr_set_debug_checks(before)
+    out_off, st_off, ring_off = H.gpu_verify(w)
+    assert np.array_equal(out_on.view(np.uint32), out_off.view(np.uint32))
+    assert np.array_equal(st_on, st_off) and np.array_equal(ring_on, ring_off)
+    assert np.array_equal(fold_on, H.gpu_fold(w, st_off, ring_off, w["accepted"]))
+    assert np.array_equal(fs, H.gpu_fwd(w)[1]) and np.array_equal(fo, H.gpu_fwd(w)[0])
+    o_off, s_off, i_off = H.gpu_fused(g)
+    assert np.array_equal(o_on, o_off) and np.array_equal(s_on, s_off)
+    assert np.array_equal(i_on, i_off)
+    say("debug index checks: rejections before launch, valid calls unchanged")
 
 
 # ------------------------------------------------------------- degenerate ---
