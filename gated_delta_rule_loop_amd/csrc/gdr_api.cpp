@@ -616,7 +616,8 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     if (!dims_built(K, V, true))
         return fail(GDR_ERR_UNSUPPORTED, "%s: head dims K=%lld V=%lld not built (%s)", fn,
                     static_cast<long long>(K), static_cast<long long>(V), kDimsBuilt);
-    if ((rc = check_layout(fn, "q", q, 1)) || (rc = check_layout(fn, "k", k, 1)) ||
+    if ((rc = check_layout(fn, "q", q, vec_mult(work))) ||
+        (rc = check_layout(fn, "k", k, vec_mult(work))) ||
         (rc = check_layout(fn, "v", v, vec_mult(work))))
         return rc;
     const int64_t gshape[3] = {B, T, HV};

@@ -74,6 +74,21 @@ __device__ __forceinline__ float sum_row_groups(float x) {
     return x;
 }
 
+// Sum over aligned groups of N adjacent lanes (N = 2..64, a power of two),
+// identical in every lane of a group: the pairs are added in the order
+// lane^1, then quads, then half-rows (8), rows (16), 32 and 64 lanes.
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+    static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "lane group");
+    x = x + dpp<0xB1>(x);                     // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (N >= 4) x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (N >= 8) x = x + dpp<0x141>(x);  // row_half_mirror: quads uniform, pairs quad 0/1
+    if constexpr (N >= 16) x = x + dpp<0x140>(x); // row_mirror: half-rows uniform, pairs them
+    if constexpr (N >= 32) x = xor16_sum(x);
+    if constexpr (N >= 64) x = xor32_sum(x);
+    return x;
+}
+
 // Several columns at once in the row-groups-high layout, same pairs and
 // association as sum_row_groups<false> (so the same bits): after the DPP step
 // each permlane swap carries two columns - a swap of (a, b) followed by one add
@@ -130,17 +145,6 @@ __device__ __forceinline__ void spread_to_all(const float (&y)[kSpread<CPL>], fl
             both16(__uint_as_float(r[1]), x[4 * i + 2], x[4 * i + 3]);
         }
     }
-}
-
-// Sum over the whole wave, identical in every lane.
-__device__ __forceinline__ float sum_wave(float x) {
-    x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-    x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-    x = x + dpp<0x141>(x);  // row_half_mirror: quads are uniform, pairs quad 0/1
-    x = x + dpp<0x140>(x);  // row_mirror: half-rows are uniform, pairs them
-    x = xor16_sum(x);
-    x = xor32_sum(x);
-    return x;
 }
 
 // ------------------------------------------------------------- bf16 I/O ---
@@ -329,6 +333,17 @@ __device__ __forceinline__ void widen_cols(const RawCols<uint16_t, CPL>& r, floa
     }
 }
 
+// The lane index as a value the compiler may not hoist (when HIDE): the
+// stage code derives addresses from it, and computing them where they are
+// used (once per stage) keeps them out of the registers that the token loop
+// needs.  Only the short-row shapes, whose token loop fills the register
+// budget, ask for it.
+template <bool HIDE>
+__device__ __forceinline__ int fresh_lane(int lane) {
+    if constexpr (HIDE) asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 // ---------------------------------------------------- per-lane arithmetic ---
 
 // The state of one (row, value head) is held as scale * S: a token's decay
@@ -413,6 +428,30 @@ __device__ __forceinline__ void ring_put(const RecParams& p, int64_t i, float x)
         static_cast<float*>(p.ring)[i] = x;
 }
 
+// N consecutive ring elements (16-byte aligned runs: N float32 or N bf16).
+template <int N>
+__device__ __forceinline__ void ring_put_run(const RecParams& p, int64_t i, const float (&x)[N]) {
+    if (p.ring_bf16) {
+        uint16_t* r = static_cast<uint16_t*>(p.ring) + i;
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int j = 0; j < N; j += 8)
+                store_cols<8>(r + j, x + j);
+        } else {
+            store_cols<N>(r, x);
+        }
+    } else {
+        float* r = static_cast<float*>(p.ring) + i;
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < N; j += 4)
+                store_cols<4>(r + j, x + j);
+        } else {
+            store_cols<N>(r, x);
+        }
+    }
+}
+
 // One work item: value columns [j0, j0 + CPL) of every key row, for one value
 // head of one row, resolved once per item.
 struct Item {
@@ -441,6 +480,78 @@ __device__ __forceinline__ float widen_raw(float raw) {
     return raw;
 }
 
+// N consecutive elements of a per-token tensor as loaded: float values, or
+// bf16 bits packed two per dword (widened after the wait, see load_raw).
+template <typename WT, int N>
+struct RawVec {
+    float v[N];
+};
+template <int N>
+struct RawVec<uint16_t, N> {
+    uint32_t v[(N + 1) / 2];
+};
+
+// N consecutive elements with the widest aligned vector loads (every caller's
+// runs are aligned to their size).
+template <int N>
+__device__ __forceinline__ void load_vec(const float* p, RawVec<float, N>& r) {
+    static_assert(N == 2 || N % 4 == 0, "float runs of 2 or 4k");
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(p + i);
+            r.v[i] = w.x; r.v[i + 1] = w.y; r.v[i + 2] = w.z; r.v[i + 3] = w.w;
+        }
+    } else {
+        const float2 w = *reinterpret_cast<const float2*>(p);
+        r.v[0] = w.x; r.v[1] = w.y;
+    }
+}
+template <int N>
+__device__ __forceinline__ void load_vec(const uint16_t* p, RawVec<uint16_t, N>& r) {
+    static_assert(N == 2 || N == 4 || N % 8 == 0, "bf16 runs of 2, 4 or 8k");
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; i += 4) {
+            const uint4 w = *reinterpret_cast<const uint4*>(p + 2 * i);
+            r.v[i] = w.x; r.v[i + 1] = w.y; r.v[i + 2] = w.z; r.v[i + 3] = w.w;
+        }
+    } else if constexpr (N == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        r.v[0] = w.x; r.v[1] = w.y;
+    } else {
+        r.v[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+}
+template <int N>
+__device__ __forceinline__ void widen_vec(const RawVec<float, N>& r, float (&o)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] = r.v[i];
+}
+template <int N>
+__device__ __forceinline__ void widen_vec(const RawVec<uint16_t, N>& r, float (&o)[N]) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        o[2 * i] = bf16_lo(r.v[i]);
+        o[2 * i + 1] = bf16_hi(r.v[i]);
+    }
+}
+// N consecutive floats to LDS (16-byte stores where N allows; the callers'
+// offsets keep them aligned).
+template <int N>
+__device__ __forceinline__ void lds_put(float* dst, const float (&x)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4)
+            *reinterpret_cast<float4*>(dst + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) dst[i] = x[i];
+    }
+}
+
 // ST: state storage type; WT: per-token input/output type (float, or
 // uint16_t holding bf16 bits).  Arithmetic is float32 either way.
 template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT>
@@ -449,19 +560,39 @@ struct Rec {
     static constexpr int BV = kLanesPerRow * CPL;
     static constexpr int TILES = V / BV;
     static constexpr int KP = K + 4 * kRowGroups;      // padded staged vector
-    static constexpr int QK = (K + 63) / 64;           // q/k elements per lane (norm)
-    static constexpr int SPW = (C + WPG - 1) / WPG;    // tokens normalised per wave
+    // L2 norms.  A token's q (or k) is split into NCH chunks of 4 elements;
+    // a lane sums the squares of its chunk in element order, and the chunk
+    // sums of a token are added by sum_lanes<NCH> - an order that depends on
+    // K only, so every launch shape normalises identically.  A norm job is one
+    // wave's worth of (token, tensor) units, lane = NCH * unit + chunk with
+    // unit = 2 * token + (0 for k, 1 for q); the stage's jobs are spread over
+    // the waves.
+    // multi-token stages in the row-groups-high layout: the token loop uses
+    // nearly the whole register budget (see fresh_lane)
+    static constexpr bool kTightRegs = C > 1 && !KG_LOW;
+    static constexpr int NCH = K / 4;                         // chunks per vector
+    static constexpr int UPJ = 64 / NCH;                      // units per job
+    static constexpr int NJOB = (2 * C + UPJ - 1) / UPJ;      // jobs per stage
+    // One-token stages: every wave normalises the token itself into its own
+    // copy of the staged k_hat and q_hat, so a wave needs no other wave's
+    // work and the workgroup needs no barrier (see stage_sync).
+    static constexpr bool kPrivStage = C == 1;
+    static constexpr int JPW = kPrivStage ? NJOB : (NJOB + WPG - 1) / WPG;  // jobs per wave
+    static constexpr int NKQ = kPrivStage ? WPG : 1;          // copies of k_hat, q_hat
+    static_assert(K % 4 == 0 && NCH <= 64, "norm chunks");
     static constexpr int VTOT = C * BV;                // v floats per wave per chunk
     static constexpr int VPL = VTOT >= 64 ? VTOT / 64 : 1;
     static_assert(R >= 2 && TILES >= 1 && V % BV == 0, "tile shape");
     static_assert(VTOT < 64 || VTOT % 64 == 0, "v staging");
     static_assert(C <= 64, "gate staging uses one lane per token");
 
-    // LDS: two chunk buffers of [k_hat C x KP | q_hat*scale C x KP | v | a |
-    // beta | per-column beta (kBetaCols only)].
+    // LDS: two chunk buffers of [NKQ x (k_hat C x KP | q_hat*scale C x KP) |
+    // v | a | beta | per-column beta (kBetaCols only)]; wave w reads the
+    // k_hat/q_hat copy at kq(w).
     static constexpr int OFF_K = 0;
     static constexpr int OFF_Q = C * KP;
-    static constexpr int OFF_V = 2 * C * KP;
+    static constexpr int OFF_V = 2 * C * KP * NKQ;
+    __device__ static int kq(int w) { return kPrivStage ? w * 2 * C * KP : 0; }
     static constexpr int OFF_A = OFF_V + WPG * VTOT;
     static constexpr int OFF_B = OFF_A + WPG * C;
     static constexpr int OFF_BV = (OFF_B + WPG * C + 3) / 4 * 4;
@@ -469,7 +600,8 @@ struct Rec {
     static constexpr int buf() { return BC ? OFF_BV + WPG * VTOT : OFF_BV; }
 
     struct Stage {
-        float q[SPW][QK], k[SPW][QK], v[VPL], bv[VPL], a, b;
+        RawVec<WT, 4> qk[JPW];
+        float v[VPL], bv[VPL], a, b;
     };
 
     // Lane = 8 * column chunk + row group (KG_LOW) or 8 * row group + column
@@ -577,66 +709,59 @@ struct Rec {
 
     // v, or the per-column beta, of a chunk: VPL consecutive elements per
     // lane of the wave's C x BV block (one vector load).  Lanes past the block
-    // or the row re-read a valid vector and keep zeros.
+    // or the row re-read a valid vector; those values are never read from
+    // the stage (the token loop stops at the row's end).
     __device__ static void load_block(const WT* base, int64_t tok, int L, int tc, int lane,
                                       float (&dst)[VPL]) {
         const int flat = min(lane * VPL, VTOT - VPL);
         const int tau = flat / BV;
         const int col = flat - tau * BV;
-        const int t = tc + tau;
-        const bool ok = lane * VPL < VTOT && t < L;
-        float x[VPL];
-        load_cols<VPL>(base + min(t, L - 1) * tok + col, x);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) dst[i] = ok ? x[i] : 0.0f;
+        load_cols<VPL>(base + min(tc + tau, L - 1) * tok + col, dst);
     }
 
     // Global loads of chunk c of an item into registers.  Each load is
-    // unconditional - an index past the row's end or the head dim is clamped
-    // to a valid element whose value is then replaced - so that a stage's
-    // loads issue back to back and retire under a single wait.  The decay is
-    // kept raw (exp is applied in commit_stage, after that wait).
+    // unconditional - an index past the row's end, the stage or the head dim
+    // is clamped to a valid element - and nothing here depends on a loaded
+    // value, so a stage's loads issue back to back and retire under a single
+    // wait in commit_stage.  Values loaded for positions past the row or the
+    // stage are never read.  The decay is kept raw (exp is applied in
+    // commit_stage).
     template <bool BC>
     __device__ static void load_stage(const RecParams& p, const Item& it, int c, Stage& s,
                                       int w, int lane) {
         const int tc = c * C;
         const int last = it.L - 1;
+        lane = fresh_lane<kTightRegs>(lane);
+        const int chunk = lane % NCH;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int tau = w + i * WPG;
-            const int t = tc + tau;
-            const int64_t tl = min(t, last);
-            const WT* qp = static_cast<const WT*>(p.q) + it.rq + tl * p.q_tok + it.h * p.q_head;
-            const WT* kp = static_cast<const WT*>(p.k) + it.rk + tl * p.k_tok + it.h * p.k_head;
-#pragma unroll
-            for (int e = 0; e < QK; ++e) {
-                const int idx = lane + 64 * e;
-                const bool in = tau < C && t < it.L && idx < K;
-                float q = 0.0f, k = 0.0f;  // raw (see load_raw); 0 is 0 either way
-                if (tau < C) {  // wave-uniform: waves past the chunk load nothing
-                    q = load_raw(qp + min(idx, K - 1));
-                    k = load_raw(kp + min(idx, K - 1));
-                }
-                s.q[i][e] = in ? q : 0.0f;
-                s.k[i][e] = in ? k : 0.0f;
-            }
+        for (int i = 0; i < JPW; ++i) {
+            const int job = kPrivStage ? i : w + i * WPG;  // wave-uniform
+            if (job >= NJOB) break;
+            const int unit = job * UPJ + lane / NCH;
+            const int tau = unit >> 1;
+            const int64_t tl = min(tc + tau, last);
+            // Lanes of units past the stage or the row load the row's last
+            // token instead; their results stay in their own lanes and are
+            // never written.
+            const WT* src = (unit & 1)
+                                ? static_cast<const WT*>(p.q) + it.rq + tl * p.q_tok + it.h * p.q_head
+                                : static_cast<const WT*>(p.k) + it.rk + tl * p.k_tok + it.h * p.k_head;
+            load_vec<4>(src + chunk * 4, s.qk[i]);
         }
         load_block(static_cast<const WT*>(p.v) + it.rv + it.hv * p.v_head + it.vt * BV, p.v_tok,
                    it.L, tc, lane, s.v);
         if constexpr (BC)
             load_block(static_cast<const WT*>(p.beta) + it.rb + it.hv * p.b_head + it.vt * BV,
                        p.b_tok, it.L, tc, lane, s.bv);
-        const bool ok = lane < C && tc + lane < it.L;
         const int64_t tl = min(tc + min(lane, C - 1), last);
-        // raw gates; an absent or out-of-range gate stages the raw form of 1
-        // (of 0 for a log decay, exp(0) = 1)
-        float g = 0.0f, b = 0.0f;
+        // raw gates; an absent gate stages the raw form of 1 (of 0 for a log
+        // decay, exp(0) = 1)
+        s.a = p.gate_is_log ? 0.0f : raw_one();
+        s.b = raw_one();
         if (p.gate)
-            g = load_raw(static_cast<const WT*>(p.gate) + it.rg + tl * p.g_tok + it.hv * p.g_head);
+            s.a = load_raw(static_cast<const WT*>(p.gate) + it.rg + tl * p.g_tok + it.hv * p.g_head);
         if (!BC && p.beta)
-            b = load_raw(static_cast<const WT*>(p.beta) + it.rb + tl * p.b_tok + it.hv * p.b_head);
-        s.a = ok && p.gate ? g : (p.gate_is_log ? 0.0f : raw_one());
-        s.b = ok && !BC && p.beta ? b : raw_one();
+            s.b = load_raw(static_cast<const WT*>(p.beta) + it.rb + tl * p.b_tok + it.hv * p.b_head);
     }
 
     // Norms of the staged tokens, then k_hat, q_hat*scale, v and gates to LDS.
@@ -648,40 +773,40 @@ struct Rec {
         const int64_t rec = it.record ? static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
                                             static_cast<int64_t>(it.h) * p.ring_head
                                       : 0;
+        lane = fresh_lane<kTightRegs>(lane);
+        const int chunk = lane % NCH;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int tau = w + i * WPG;
-            if (tau >= C) break;
-            float qv[QK], kv[QK];
-#pragma unroll
-            for (int e = 0; e < QK; ++e) {
-                qv[e] = widen_raw<WT>(s.q[i][e]);
-                kv[e] = widen_raw<WT>(s.k[i][e]);
-            }
-            float rk = 1.0f, rqs = p.scale;
+        for (int i = 0; i < JPW; ++i) {
+            const int job = kPrivStage ? i : w + i * WPG;  // wave-uniform
+            // tokens past the row's end are never read from the stage
+            if (job >= NJOB || tc + (job * UPJ) / 2 >= it.L) break;
+            const int unit = job * UPJ + lane / NCH;
+            const bool is_q = unit & 1;
+            const int tau = unit >> 1;
+            float x[4];
+            widen_vec(s.qk[i], x);
+            float f = is_q ? p.scale : 1.0f;
             if (p.l2norm) {
-                float kk = kv[0] * kv[0];
-                float qq = qv[0] * qv[0];
+                float ss = x[0] * x[0];
 #pragma unroll
-                for (int e = 1; e < QK; ++e) {
-                    kk = __builtin_fmaf(kv[e], kv[e], kk);
-                    qq = __builtin_fmaf(qv[e], qv[e], qq);
-                }
-                kk = sum_wave(kk);
-                qq = sum_wave(qq);
-                rk = rsqrtf(kk + kEps);
-                rqs = rsqrtf(qq + kEps) * p.scale;
+                for (int e = 1; e < 4; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+                ss = sum_lanes<NCH>(ss);
+                const float r = rsqrtf(ss + kEps);
+                f = is_q ? r * p.scale : r;
             }
-            const bool rec_k = it.record && it.part == 0 && tc + tau < it.L;
+            if (tau < C) {
 #pragma unroll
-            for (int e = 0; e < QK; ++e) {
-                const int idx = lane + 64 * e;
-                if (idx < K) {
-                    const float kh = kv[e] * rk;
-                    B[OFF_K + tau * KP + stage_pos<R>(idx)] = kh;
-                    B[OFF_Q + tau * KP + stage_pos<R>(idx)] = qv[e] * rqs;
-                    if (rec_k) ring_put(p, rec + (tc + tau) * p.ring_tok + idx, kh);
+                for (int e = 0; e < 4; ++e) x[e] = x[e] * f;
+                float* dst = B + kq(w) + (is_q ? OFF_Q : OFF_K) + tau * KP;
+                if constexpr (R % 4 == 0) {
+                    lds_put<4>(dst + stage_pos<R>(chunk * 4), x);
+                } else {  // R == 2: the chunk spans two row groups
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[stage_pos<R>(chunk * 4 + e)] = x[e];
                 }
+                if (!is_q && it.record && it.part == 0 && (!kPrivStage || w == 0) &&
+                    tc + tau < it.L)
+                    ring_put_run<4>(p, rec + (tc + tau) * p.ring_tok + chunk * 4, x);
             }
         }
 #pragma unroll
@@ -751,8 +876,9 @@ struct Rec {
         const int r16 = lane >> 4;
         auto scol = [&](int i) { return (CPL == 2 ? (r16 & 1) : r16) + 4 * i; };
         const bool spread_lead = (lane & 8) == 0 && (CPL != 2 || lane < 32);
+        const float* KQ = B + kq(w);  // this wave's k_hat / q_hat copy
         float kr[R];
-        read_rows<R>(B + OFF_K, kg, kr);
+        read_rows<R>(KQ + OFF_K, kg, kr);
         float x[CPL];                 // S^T k_hat of the current token, before the scale
         float xs[kSpread<CPL>];       // the same, spread (kSpreadOut)
         dot_rows<R, CPL>(S, kr, x);
@@ -801,11 +927,11 @@ struct Rec {
             }
 
             float qr[R];
-            read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
+            read_rows<R>(KQ + OFF_Q + tau * KP, kg, qr);
             float o[CPL];
             dot_rows<R, CPL>(S, qr, o);
             if (C > 1 && tau + 1 < Lc) {
-                read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
+                read_rows<R>(KQ + OFF_K + (tau + 1) * KP, kg, kr);
                 dot_rows<R, CPL>(S, kr, x);
                 if constexpr (kSpreadOut) sum_cols_spread<CPL>(x, xs);
                 else sum_cols_all(x);
@@ -876,6 +1002,19 @@ struct Rec {
     // stages fit three workgroups per CU.
     static constexpr int kStageBufs = KG_LOW ? 1 : 2;
 
+    // A committed stage becomes readable: a workgroup barrier, or for the
+    // one-token stages (each wave reads only what it wrote) the wave's own
+    // LDS writes completing before its lanes read each other's values.
+    __device__ static void stage_sync() {
+        if constexpr (kPrivStage) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else {
+            __syncthreads();
+        }
+    }
+
     // All chunks of an item whose loaded state is rs and whose chunk-0 inputs
     // are in st; leaves the final state as scale * S.  The state is widened
     // after the first stage is committed, so its loads complete under that
@@ -887,7 +1026,7 @@ struct Rec {
         constexpr bool BC = (MODE & kBetaCols) != 0;
         constexpr int BUF = buf<BC>();
         commit_stage<BC>(p, it, 0, st, lds, w, lane);
-        __syncthreads();
+        stage_sync();
         __builtin_amdgcn_sched_barrier(0);  // keep the widening (and its wait) here
         widen_state(rs, S);
         scale = 1.0f;
@@ -908,7 +1047,7 @@ struct Rec {
                 if constexpr (kStageBufs == 1) __syncthreads();  // the stage has been read
                 commit_stage<BC>(p, it, c + 1, st, lds + (kStageBufs == 2 ? ((c + 1) & 1) * BUF : 0),
                                  w, lane);
-                __syncthreads();
+                stage_sync();
             }
         }
     }

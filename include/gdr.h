@@ -26,8 +26,8 @@
  *     qkv_conv_output, recurrence_output, the fused update's q, k, v, o and
  *     per-column beta, and the Conv1d's x, out and history.  Their outer
  *     strides must keep 16-byte rows (multiples of 4 elements for float32
- *     and of 8 for bfloat16), except the fused q and k (any outer stride)
- *     and the Conv1d tensors (multiples of 4 elements in either dtype).
+ *     and of 8 for bfloat16), except the Conv1d tensors (multiples of 4
+ *     elements in either dtype).
  *     Per-token gates (decay, beta, g, head-wise beta) take any strides;
  *     index vectors of more than one element must be contiguous.
  *   - Return value: GDR_OK, or a negative GDR_ERR_* code with a message
