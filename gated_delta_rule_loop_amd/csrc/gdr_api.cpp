@@ -274,17 +274,16 @@ float resolve_scale(float scale, int64_t K) {
 // not depend on this choice.
 enum class Entry { Packed, Fused, Fold };
 
-// Longest rows first for ragged short-row batches (multi-token stages, row
-// groups in the high lane bits: the verify and short-window shapes) small
-// enough for every workgroup to rank the rows itself, when the grid is larger
-// than what one pass of the chip holds at once (256 compute units, about 4
-// workgroups each): a grid that is resident as a whole gains nothing from the
-// order.  The long-row shapes run without it (their code is compiled without
-// the ranking).
+// Longest rows first for ragged multi-token batches small enough for every
+// workgroup to rank the rows itself: for the short-row shapes (row groups in
+// the high lane bits: verify windows) when the grid is larger than what one
+// pass of the chip holds at once (256 compute units, about 4 workgroups
+// each); for the long-row shapes always, because their rows share compute
+// units with one another and the longest should start first.
 int32_t order_rows(const gdr::LaunchShape& s, const gdr::RecParams& p) {
     const int64_t grid = int64_t{p.rows} * p.nk * p.parts;
     return p.offsets != nullptr && p.rows >= 2 && p.rows <= gdr::kOrderMaxRows &&
-           s.chunk > 1 && !s.kg_low && grid > 4 * 256;
+           s.chunk > 1 && (s.kg_low || grid > 4 * 256);
 }
 
 gdr::LaunchShape pick_shape(Entry e, int64_t K, int64_t V, int64_t G, int64_t total_tokens,

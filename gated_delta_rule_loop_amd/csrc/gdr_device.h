@@ -985,6 +985,149 @@ struct Rec {
         }
     }
 
+    // Both K-reductions of a token in one pass over the registers, their
+    // chains interleaved: o = S^T q and x = S^T k, each in the order of
+    // dot_rows (so the same bits).
+    __device__ static void dot_rows2(const float (&S)[R][CPL], const float (&qv)[R],
+                                     const float (&kv)[R], float (&o)[CPL], float (&x)[CPL]) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            o[c] = S[0][c] * qv[0];
+            x[c] = S[0][c] * kv[0];
+        }
+#pragma unroll
+        for (int ri = 1; ri < R; ++ri)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                o[c] = __builtin_fmaf(S[ri][c], qv[ri], o[c]);
+                x[c] = __builtin_fmaf(S[ri][c], kv[ri], x[c]);
+            }
+    }
+
+    // True when no token of the stage can take the running scale out of
+    // [2^-64, 2^64], so the tokens may skip decay_step's test: every decay is
+    // positive and finite and the exact products scale * a_1 * ... * a_t stay
+    // within [2^-62, 2^62] (the float32 products differ from them by far less
+    // than a factor of 2).  Lane t holds log2 of token t's decay and the lanes
+    // form prefix sums; wave-uniform.
+    __device__ static bool stage_in_range(const float* A, int Lc, float scale, int lane) {
+        bool bad = false;
+        float l = 0.0f;
+        if (lane < Lc) {
+            const float a = A[lane];
+            bad = !(a > 0.0f && a < __builtin_inff());  // zero, negative, inf or NaN
+            l = __builtin_amdgcn_logf(a);                // log2
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            if (d >= C) break;
+            const float y = __shfl_up(l, d);
+            if (lane >= d) l += y;
+        }
+        const float ls = __builtin_amdgcn_logf(scale);
+        const bool ok = lane >= Lc || (!bad && l + ls >= -62.0f && l + ls <= 62.0f);
+        return __ballot(!ok) == 0;
+    }
+
+    // The tokens of a long-row stage (row groups in the low lane bits): as
+    // run_chunk, with the next token's retrieval computed unconditionally in
+    // the same register pass as this token's read-out (after the stage's last
+    // token it reads a stale k_hat slot and the value is discarded), and the
+    // decay range test made once per stage when CHECK is false.
+    template <bool CHECK, bool REC, bool SNAP, bool BC>
+    __device__ static void long_tokens(const RecParams& p, const Item& it, int tc, int Lc,
+                                       const float* B, float (&S)[R][CPL], float& scale,
+                                       float (&kr)[R], float (&x)[CPL], int w, int lane) {
+        const int kg = row_group(lane);
+        const int vc = col_chunk(lane) * CPL;
+        WT* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
+        int64_t rec = 0;
+        if (REC && it.record)
+            rec = static_cast<int64_t>(p.ring_idx[it.row]) * p.ring_row +
+                  static_cast<int64_t>(it.h) * p.ring_head + static_cast<int64_t>(tc) * p.ring_tok;
+        ST* snap = nullptr;
+        int snap_left = 0;
+        if constexpr (SNAP) {
+            snap_left = p.spt - tc % p.spt;
+            snap = static_cast<ST*>(p.snap) + static_cast<int64_t>(it.slot) * p.snap_slot +
+                   static_cast<int64_t>(tc / p.spt) * p.snap_tok +
+                   static_cast<int64_t>(it.hv) * p.snap_head + it.j0;
+        }
+        int snap_i = SNAP ? tc / p.spt : 0;
+#pragma unroll 2
+        for (int tau = 0; tau < Lc; ++tau) {
+            const float a = B[OFF_A + w * C + tau];
+            const float b = BC ? 1.0f : B[OFF_B + w * C + tau];
+            const float cn = scale * a;
+            float u[CPL], us[CPL];
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float vv = B[OFF_V + w * VTOT + tau * BV + vc + cc];
+                const float be = BC ? B[OFF_BV + w * VTOT + tau * BV + vc + cc] : b;
+                u[cc] = be * (vv - cn * x[cc]);
+            }
+            scale = CHECK ? decay_step<R, CPL>(S, cn) : cn;
+            const float rho = __builtin_amdgcn_rcpf(scale);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) us[cc] = u[cc] * rho;
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+                for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us[cc], S[ri][cc]);
+            float qr[R], o[CPL];
+            read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
+            read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
+            dot_rows2(S, qr, kr, o, x);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                o[cc] = scale * sum_row_groups<true>(o[cc]);
+                x[cc] = sum_row_groups<true>(x[cc]);
+            }
+            // every lane holds its columns' totals: the 8 lanes of a column
+            // store the same bits to the same address
+            store_cols<CPL>(outp, o);
+            outp += p.o_tok;
+            if (REC && it.record) {
+                const int64_t ru = rec + K + it.m * V + it.j0;
+                if (kg == 0) {
+                    if (p.ring_bf16)
+                        store_cols<CPL>(static_cast<uint16_t*>(p.ring) + ru, u);
+                    else
+                        store_cols<CPL>(static_cast<float*>(p.ring) + ru, u);
+                }
+                if (it.vt == 0 && lane == 0) ring_put(p, rec + K + p.G * V + it.m, a);
+                rec += p.ring_tok;
+            }
+            if constexpr (SNAP) {
+                if (--snap_left == 0) {
+                    snap_left = p.spt;
+                    if (snap_i < p.snap_count) store_tile(snap, kg, scale, S);
+                    ++snap_i;
+                    snap += p.snap_tok;
+                }
+            }
+        }
+    }
+
+    template <bool REC, bool SNAP, bool BC>
+    __device__ static void run_chunk_long(const RecParams& p, const Item& it, int c,
+                                          const float* B, float (&S)[R][CPL], float& scale,
+                                          int w, int lane) {
+        static_assert(KG_LOW, "long-row layout");
+        const int kg = row_group(lane);
+        const int tc = c * C;
+        const int Lc = __builtin_amdgcn_readfirstlane(min(C, it.L - tc));
+        float kr[R], x[CPL];
+        read_rows<R>(B + OFF_K, kg, kr);
+        dot_rows<R, CPL>(S, kr, x);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<true>(x[cc]);
+        if (stage_in_range(B + OFF_A + w * C, Lc, scale, lane))
+            long_tokens<false, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
+        else
+            long_tokens<true, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
+    }
+
     // MODE: kPlain (forward, fused update without snapshots), kVerify (rows
     // that fit the ring record it; longer rows run as kPlain), kSnap; with
     // kBetaCols, beta is read per value column.
@@ -992,8 +1135,12 @@ struct Rec {
     __device__ static void run_chunk_mode(const RecParams& p, const Item& it, int c,
                                           const float* B, float (&S)[R][CPL], float& scale, int w,
                                           int lane) {
-        run_chunk<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
-            p, it, c, B, S, scale, w, lane);
+        if constexpr (KG_LOW)
+            run_chunk_long<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
+                p, it, c, B, S, scale, w, lane);
+        else
+            run_chunk<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
+                p, it, c, B, S, scale, w, lane);
     }
 
     // Stage buffers in LDS: two for the short-row shapes (the next stage is
@@ -1061,9 +1208,17 @@ struct Rec {
 // ballot scan for the k-th row of the rank's bucket.  Called by every thread
 // of the workgroup (two barriers) with kOrderBuckets + B words of LDS;
 // returns a wave-uniform row in [0, B).
+// Length buckets: one per length below 32, then four per octave (the two
+// bits after the leading one) up to 8191; longer rows share the last.  Bucket
+// 0 holds the longest rows.
 __device__ inline uint32_t order_bucket(uint32_t len) {
+    uint32_t b = len;
+    if (len >= 32) {
+        const uint32_t e = 31 - __builtin_clz(len);  // floor(log2(len)) >= 5
+        b = 32 + 4 * (e - 5) + ((len >> (e - 2)) & 3);
+    }
     const uint32_t top = kOrderBuckets - 1;
-    return top - (len < top ? len : top);  // bucket 0 holds the longest rows
+    return top - (b < top ? b : top);
 }
 
 __device__ int ordered_row(const uint32_t* off, int B, int rank, uint32_t* scratch) {
@@ -1110,14 +1265,19 @@ __device__ int ordered_row(const uint32_t* off, int B, int rank, uint32_t* scrat
 // One work item per workgroup.
 // Waves per SIMD asked of the register allocator: the one-token (HBM-bound
 // decode) stages 4, or 2 at 8 columns per lane; the short-row shapes of at most
-// 4 columns at K <= 128 4 (verify window: -3.6%); the rest as many as fit.
+// 4 columns at K <= 128 4 (verify window: -3.6%); the long-row shapes at
+// K <= 128 3 (their workgroups' LDS allows 3 per CU); the rest as many as fit.
 template <int K, int C, int CPL, bool KG_LOW>
-constexpr int kMinWaves = C == 1 ? (CPL <= 4 ? 4 : 2) : (!KG_LOW && K <= 128 && CPL <= 4 ? 4 : 1);
+constexpr int kMinWaves = C == 1 ? (CPL <= 4 ? 4 : 2)
+                        : (K <= 128 && CPL <= 4 ? (KG_LOW ? (CPL == 1 ? 3 : 2) : 4) : 1);
 
 template <int K, int V, int CPL, int C, int WPG, typename ST, bool KG_LOW, typename WT, int MODE>
 __global__ void __launch_bounds__(WPG * 64, (kMinWaves<K, C, CPL, KG_LOW>)) rec_kernel(const RecParams p) {
     using Q = Rec<K, V, CPL, C, WPG, ST, KG_LOW, WT>;
-    __shared__ __attribute__((aligned(16))) float lds[Q::kStageBufs * Q::template buf<(MODE & kBetaCols) != 0>()];
+    // stage buffers, then (long-row shapes) the row ranking's words
+    constexpr int kStageWords = Q::kStageBufs * Q::template buf<(MODE & kBetaCols) != 0>();
+    constexpr int kRankWords = C > 1 && KG_LOW ? kOrderBuckets + kOrderMaxRows : 0;
+    __shared__ __attribute__((aligned(16))) float lds[kStageWords + kRankWords];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int kg = Q::row_group(lane);
@@ -1130,15 +1290,16 @@ __global__ void __launch_bounds__(WPG * 64, (kMinWaves<K, C, CPL, KG_LOW>)) rec_
         const int q = idx >> 3;
         idx = ((q / p.parts) * 8 + (idx & 7)) * p.parts + q % p.parts;
     }
-    if (C > 1 && !KG_LOW && p.order) {  // set for the multi-token row-groups-high shapes only
+    if (C > 1 && p.order) {  // set for multi-token shapes only
         const int per_row = p.parts * p.nk;
         const int rank = idx / per_row;
-        // The ranking's LDS is the second stage buffer: the first write there
-        // (chunk 1's commit) comes after a barrier that every wave reaches
-        // only once it has ranked.
+        // The short-row shapes rank in their second stage buffer: the first
+        // write there (chunk 1's commit) comes after a barrier that every wave
+        // reaches only once it has ranked.  The long-row shapes (one stage
+        // buffer) rank in words of their own.
         constexpr int BUF = Q::template buf<(MODE & kBetaCols) != 0>();
         static_assert(C == 1 || KG_LOW || BUF >= kOrderBuckets + kOrderMaxRows, "ranking LDS");
-        uint32_t* scratch = reinterpret_cast<uint32_t*>(lds + BUF);
+        uint32_t* scratch = reinterpret_cast<uint32_t*>(lds + (KG_LOW ? kStageWords : BUF));
         const int row = __builtin_amdgcn_readfirstlane(ordered_row(p.offsets, p.rows, rank, scratch));
         idx = row * per_row + (idx - rank * per_row);
     }

@@ -47,9 +47,9 @@ struct RecParams {
     int32_t order;   // 1: workgroups take the rows longest first (offsets, <= kOrderMaxRows rows)
 };
 
-// Longest-first row order: lengths are bucketed (kOrderBuckets buckets, the
-// last one holding every length >= kOrderBuckets - 1), and every workgroup
-// ranks the rows itself, so it is offered for small batches only.
+// Longest-first row order: lengths are bucketed (kOrderBuckets buckets, exact
+// below 32 tokens and four per octave above), and every workgroup ranks the
+// rows itself, so it is offered for small batches only.
 constexpr int kOrderBuckets = 64;
 constexpr int kOrderMaxRows = 256;
 
@@ -122,7 +122,7 @@ constexpr bool kShortKgLow = false;
 constexpr int kFusedCpl = 8;
 constexpr int kFusedChunk = 4;
 constexpr bool kFusedKgLow = false;
-constexpr int kLongCpl = 1;
+constexpr int kLongCpl = 2;
 constexpr int kLongChunk = 32;
 constexpr bool kLongKgLow = true;
 constexpr int kFoldCpl = 4;
