@@ -436,6 +436,9 @@ int packed_walk(const char* fn, int32_t nv, int32_t nk, const gdr_tensor* out,
     p.nk = nk;
     p.G = static_cast<int32_t>(G);
     p.parts = static_cast<int32_t>(units / s.wpg);
+    p.div_parts = gdr::make_fastdiv(static_cast<uint32_t>(p.parts));
+    p.div_nk = gdr::make_fastdiv(static_cast<uint32_t>(p.nk));
+    p.div_row = gdr::make_fastdiv(static_cast<uint32_t>(p.parts * p.nk));
     if (int64_t{p.rows} * p.nk * p.parts > INT32_MAX)
         return fail(GDR_ERR_INVALID_ARG, "%s: batch too large for one launch", fn);
     p.offsets = as_u32(offsets);
@@ -714,6 +717,9 @@ int gdr_fused_recurrent_update(const gdr_tensor* q, const gdr_tensor* k, const g
     p.nk = static_cast<int32_t>(H);
     p.G = static_cast<int32_t>(G);
     p.parts = static_cast<int32_t>(units / s.wpg);
+    p.div_parts = gdr::make_fastdiv(static_cast<uint32_t>(p.parts));
+    p.div_nk = gdr::make_fastdiv(static_cast<uint32_t>(p.nk));
+    p.div_row = gdr::make_fastdiv(static_cast<uint32_t>(p.parts * p.nk));
     if (int64_t{p.rows} * p.nk * p.parts > INT32_MAX)
         return fail(GDR_ERR_INVALID_ARG, "%s: batch too large for one launch", fn);
     p.dense_len = static_cast<int32_t>(T);

@@ -344,6 +344,12 @@ __device__ __forceinline__ int fresh_lane(int lane) {
     return lane;
 }
 
+// x / d for x < 2^31 (see FastDiv).
+__device__ __forceinline__ int fdiv(int x, FastDiv f) {
+    const uint32_t u = static_cast<uint32_t>(x);
+    return static_cast<int>((__umulhi(u, f.mul) + u) >> f.shift);
+}
+
 // ---------------------------------------------------- per-lane arithmetic ---
 
 // The state of one (row, value head) is held as scale * S: a token's decay
@@ -612,11 +618,10 @@ struct Rec {
 
     __device__ static Item item(const RecParams& p, int idx, int w, int lane) {
         Item it;
-        int blk = idx;
-        it.part = blk % p.parts;
-        blk /= p.parts;
-        it.h = blk % p.nk;
-        it.row = blk / p.nk;
+        const int blk = fdiv(idx, p.div_parts);
+        it.part = idx - blk * p.parts;
+        it.row = fdiv(blk, p.div_nk);
+        it.h = blk - it.row * p.nk;
         const int unit = it.part * WPG + w;
         it.m = unit / TILES;
         it.vt = unit - it.m * TILES;
@@ -1029,15 +1034,18 @@ struct Rec {
         return __ballot(!ok) == 0;
     }
 
-    // The tokens of a long-row stage (row groups in the low lane bits): as
-    // run_chunk, with the next token's retrieval computed unconditionally in
-    // the same register pass as this token's read-out (after the stage's last
-    // token it reads a stale k_hat slot and the value is discarded), and the
-    // decay range test made once per stage when CHECK is false.
+    // The tokens of a multi-token stage: as run_chunk, with the next token's
+    // retrieval computed unconditionally in the same register pass as this
+    // token's read-out (after the stage's last token it reads a k_hat slot
+    // that holds no token of the row and the value is discarded), and the
+    // decay range test made once per stage when CHECK is false.  x holds the
+    // retrieval of the current token: per column (row groups low), or spread
+    // (row groups high, see sum_cols_spread).
+    static constexpr int kX = kSpreadOut ? kSpread<CPL> : CPL;
     template <bool CHECK, bool REC, bool SNAP, bool BC>
-    __device__ static void long_tokens(const RecParams& p, const Item& it, int tc, int Lc,
-                                       const float* B, float (&S)[R][CPL], float& scale,
-                                       float (&kr)[R], float (&x)[CPL], int w, int lane) {
+    __device__ static void stage_tokens(const RecParams& p, const Item& it, int tc, int Lc,
+                                        const float* B, float (&S)[R][CPL], float& scale,
+                                        float (&kr)[R], float (&x)[kX], int w, int lane) {
         const int kg = row_group(lane);
         const int vc = col_chunk(lane) * CPL;
         WT* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
@@ -1054,42 +1062,72 @@ struct Rec {
                    static_cast<int64_t>(it.hv) * p.snap_head + it.j0;
         }
         int snap_i = SNAP ? tc / p.spt : 0;
-#pragma unroll 2
+        // spread form: this lane holds the totals of columns vc + scol(i)
+        const int r16 = lane >> 4;
+        auto scol = [&](int i) { return (CPL == 2 ? (r16 & 1) : r16) + 4 * i; };
+        const bool spread_lead = (lane & 8) == 0 && (CPL != 2 || lane < 32);
         for (int tau = 0; tau < Lc; ++tau) {
             const float a = B[OFF_A + w * C + tau];
             const float b = BC ? 1.0f : B[OFF_B + w * C + tau];
             const float cn = scale * a;
-            float u[CPL], us[CPL];
+            float u[kX];  // u of the lane's columns (spread: of its spread columns)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
+            for (int i = 0; i < kX; ++i) {
+                const int cc = kSpreadOut ? scol(i) : i;
                 const float vv = B[OFF_V + w * VTOT + tau * BV + vc + cc];
                 const float be = BC ? B[OFF_BV + w * VTOT + tau * BV + vc + cc] : b;
-                u[cc] = be * (vv - cn * x[cc]);
+                u[i] = be * (vv - cn * x[i]);
             }
             scale = CHECK ? decay_step<R, CPL>(S, cn) : cn;
             const float rho = __builtin_amdgcn_rcpf(scale);
+            float us[CPL];
+            if constexpr (kSpreadOut) {
+                float us_s[kX];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) us[cc] = u[cc] * rho;
+                for (int i = 0; i < kX; ++i) us_s[i] = u[i] * rho;
+                spread_to_all<CPL>(us_s, us);
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) us[cc] = u[cc] * rho;
+            }
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
                 for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us[cc], S[ri][cc]);
-            float qr[R], o[CPL];
+            float qr[R], o[CPL], xk[CPL];
             read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
             read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
-            dot_rows2(S, qr, kr, o, x);
+            dot_rows2(S, qr, kr, o, xk);
+            if constexpr (kSpreadOut) {
+                float y[kX];
+                sum_cols_spread<CPL>(o, y);
+                sum_cols_spread<CPL>(xk, x);
+                if (spread_lead) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                o[cc] = scale * sum_row_groups<true>(o[cc]);
-                x[cc] = sum_row_groups<true>(x[cc]);
+                    for (int i = 0; i < kX; ++i) {
+                        const float val = scale * y[i];
+                        store_cols<1>(outp + scol(i), &val);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    o[cc] = scale * sum_row_groups<true>(o[cc]);
+                    x[cc] = sum_row_groups<true>(xk[cc]);
+                }
+                // every lane holds its columns' totals: the 8 lanes of a
+                // column store the same bits to the same address
+                store_cols<CPL>(outp, o);
             }
-            // every lane holds its columns' totals: the 8 lanes of a column
-            // store the same bits to the same address
-            store_cols<CPL>(outp, o);
             outp += p.o_tok;
             if (REC && it.record) {
                 const int64_t ru = rec + K + it.m * V + it.j0;
-                if (kg == 0) {
+                if constexpr (kSpreadOut) {
+                    if (spread_lead) {
+#pragma unroll
+                        for (int i = 0; i < kX; ++i) ring_put(p, ru + scol(i), u[i]);
+                    }
+                } else if (kg == 0) {
                     if (p.ring_bf16)
                         store_cols<CPL>(static_cast<uint16_t*>(p.ring) + ru, u);
                     else
@@ -1109,23 +1147,29 @@ struct Rec {
         }
     }
 
+    // A multi-token stage: the retrieval of its first token, the stage-wide
+    // decay range test, then the tokens.
     template <bool REC, bool SNAP, bool BC>
-    __device__ static void run_chunk_long(const RecParams& p, const Item& it, int c,
-                                          const float* B, float (&S)[R][CPL], float& scale,
-                                          int w, int lane) {
-        static_assert(KG_LOW, "long-row layout");
+    __device__ static void run_stage(const RecParams& p, const Item& it, int c, const float* B,
+                                     float (&S)[R][CPL], float& scale, int w, int lane) {
+        static_assert(C > 1, "multi-token stages");
         const int kg = row_group(lane);
         const int tc = c * C;
         const int Lc = __builtin_amdgcn_readfirstlane(min(C, it.L - tc));
-        float kr[R], x[CPL];
+        float kr[R], x[kX];
         read_rows<R>(B + OFF_K, kg, kr);
-        dot_rows<R, CPL>(S, kr, x);
+        float xc[CPL];
+        dot_rows<R, CPL>(S, kr, xc);
+        if constexpr (kSpreadOut) {
+            sum_cols_spread<CPL>(xc, x);
+        } else {
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<true>(x[cc]);
+            for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<true>(xc[cc]);
+        }
         if (stage_in_range(B + OFF_A + w * C, Lc, scale, lane))
-            long_tokens<false, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
+            stage_tokens<false, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
         else
-            long_tokens<true, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
+            stage_tokens<true, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
     }
 
     // MODE: kPlain (forward, fused update without snapshots), kVerify (rows
@@ -1135,8 +1179,11 @@ struct Rec {
     __device__ static void run_chunk_mode(const RecParams& p, const Item& it, int c,
                                           const float* B, float (&S)[R][CPL], float& scale, int w,
                                           int lane) {
-        if constexpr (KG_LOW)
-            run_chunk_long<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
+        // the long-row shapes' tokens interleave two reductions (registers to
+        // spare); the short-row shapes' token loop fills the register budget
+        // as it is
+        if constexpr (KG_LOW && C > 1)
+            run_stage<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
                 p, it, c, B, S, scale, w, lane);
         else
             run_chunk<(MODE & 3) == kVerify, (MODE & 3) == kSnap, (MODE & kBetaCols) != 0>(
@@ -1288,11 +1335,12 @@ __global__ void __launch_bounds__(WPG * 64, (kMinWaves<K, C, CPL, KG_LOW>)) rec_
     // head) pairs still spread over all XCDs.
     if (p.parts > 1 && (p.rows * p.nk) % 8 == 0) {
         const int q = idx >> 3;
-        idx = ((q / p.parts) * 8 + (idx & 7)) * p.parts + q % p.parts;
+        const int qp = fdiv(q, p.div_parts);
+        idx = (qp * 8 + (idx & 7)) * p.parts + (q - qp * p.parts);
     }
     if (C > 1 && p.order) {  // set for multi-token shapes only
         const int per_row = p.parts * p.nk;
-        const int rank = idx / per_row;
+        const int rank = fdiv(idx, p.div_row);
         // The short-row shapes rank in their second stage buffer: the first
         // write there (chunk 1's commit) comes after a barrier that every wave
         // reaches only once it has ranked.  The long-row shapes (one stage
