@@ -556,6 +556,11 @@ int gdr_state_fold(int32_t num_value_heads, int32_t num_key_heads,
         return GDR_OK;
     }
     gdr::LaunchShape s = pick_shape(Entry::Fold, K, V, G, B, B, nv);
+    if (K == 128 && V == 128 && ring->dtype == GDR_DTYPE_BF16) {
+        s.cpl = gdr::kFoldCplBf16Ring;  // 16-byte state accesses (measured faster with a bf16 ring)
+        const int64_t units16 = G * (V / (gdr::kLanesPerRow * s.cpl));
+        s.wpg = units16 % 4 == 0 ? 4 : (units16 % 2 == 0 ? 2 : 1);
+    }
     const int64_t units = G * (V / (gdr::kLanesPerRow * s.cpl));
     gdr::FoldParams p{};
     p.rows = static_cast<int32_t>(B);

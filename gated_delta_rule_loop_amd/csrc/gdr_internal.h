@@ -140,7 +140,9 @@ constexpr bool kFusedKgLow = false;
 constexpr int kLongCpl = 2;
 constexpr int kLongChunk = 32;
 constexpr bool kLongKgLow = true;
-constexpr int kFoldCpl = 4;
+constexpr int kFoldCpl = 4;         // float32 ring
+constexpr int kFoldCplBf16Ring = 8; // bf16 ring
+constexpr int kFoldStage = 8;       // ring tokens staged in LDS per fold pass
 
 // Columns per wave for a given lanes-per-column setting.
 constexpr int kLanesPerRow = 8;   // lanes that share one key-row group

@@ -52,25 +52,20 @@ namespace {
 
 // ------------------------------------------------------------------- fold ---
 
-// R consecutive ring elements (float32 or bf16) widened to float.
-template <int R>
-__device__ __forceinline__ void load_run(const float* p, float (&out)[R]) {
-    if constexpr (R % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < R; i += 4) load_cols<4>(p + i, out + i);
-    } else {
-        load_cols<R>(p, out);
-    }
-}
-template <int R>
-__device__ __forceinline__ void load_run(const uint16_t* p, float (&out)[R]) {
-    if constexpr (R % 8 == 0) {
-#pragma unroll
-        for (int i = 0; i < R; i += 8) load_cols<8>(p + i, out + i);
-    } else {
-        load_cols<R>(p, out);
-    }
-}
+// The ring records a workgroup folds are staged in LDS, kFoldStage tokens at
+// a time, by loads issued together with the state loads: the token walk then
+// reads LDS, so a wave waits for memory once rather than once per token.
+// Staged token: the key row (padded per row group as stage_pos when the group
+// holds a multiple of 4 rows), then u and the decay of each value head the
+// workgroup covers.
+template <int K, int HW>
+struct FoldStage {
+    static constexpr int R = K / kRowGroups;
+    static constexpr bool kPad = R % 4 == 0;
+    static constexpr int kK = kPad ? K + kRowGroups * 4 : K;   // staged key row
+    static constexpr int kTok = kK + HW * K + ((HW + 3) & ~3);  // floats per token (V = K)
+    __device__ static int kpos(int idx) { return kPad ? stage_pos<R>(idx) : idx; }
+};
 
 template <int K, int CPL, int WPG, typename ST, typename RT>
 __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
@@ -78,6 +73,14 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
     constexpr int R = K / kRowGroups;
     constexpr int BV = kLanesPerRow * CPL;
     constexpr int TILES = V / BV;
+    constexpr int HW = WPG > TILES ? WPG / TILES : 1;  // value heads per workgroup
+    using FS = FoldStage<K, HW>;
+    constexpr int TCH = kFoldStage;
+    constexpr int KV = K / 4, UV = V / 4;               // 4-element runs of k and of u
+    constexpr int PER_TOK = KV + HW * UV + HW;          // loads per token (a: one each)
+    constexpr int NT = WPG * 64;
+    constexpr int ITEMS = (TCH * PER_TOK + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) float stage[TCH * FS::kTok];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -91,6 +94,7 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
     const int unit = part * WPG + w;
     const int m = unit / TILES;
     const int vt = unit - m * TILES;
+    const int m0 = (part * WPG) / TILES;  // first value head (within the key head) of the workgroup
     const int hv = h * p.G + m;
     const int j0 = vt * BV + vl * CPL;
 
@@ -100,34 +104,93 @@ __global__ void __launch_bounds__(WPG * 64) fold_kernel(const FoldParams p) {
 
     ST* sp = static_cast<ST*>(p.state) + static_cast<int64_t>(slot) * p.st_slot +
              static_cast<int64_t>(hv) * p.st_head + j0;
-    float S[R][CPL];
+    RawCols<ST, CPL> raw[R];
 #pragma unroll
-    for (int ri = 0; ri < R; ++ri) {
-        RawCols<ST, CPL> raw;
-        load_raw_cols<CPL>(sp + key_row<R>(kg, ri) * V, raw);
-        widen_cols<CPL>(raw, S[ri]);
-    }
+    for (int ri = 0; ri < R; ++ri) load_raw_cols<CPL>(sp + key_row<R>(kg, ri) * V, raw[ri]);
 
     const RT* rec = static_cast<const RT*>(p.ring) +
                     static_cast<int64_t>(p.ring_idx[row]) * p.ring_row +
                     static_cast<int64_t>(h) * p.ring_head;
-    float scale = 1.0f;
-    for (uint32_t t = 0; t < n; ++t) {
-        const RT* r = rec + static_cast<int64_t>(t) * p.ring_tok;
-        float a;
-        load_cols<1>(r + K + p.G * V + m, &a);
-        float kr[R];
-        load_run<R>(r + key_row<R>(kg, 0), kr);
-        float u[CPL];
-        load_cols<CPL>(r + K + m * V + j0, u);
-        scale = decay_step<R, CPL>(S, scale * a);
-        const float rho = __builtin_amdgcn_rcpf(scale);
+    // Stage tokens [t0, t0 + cnt) of the ring into LDS.  The thread index is
+    // re-read per stage so that the item addresses are not held across the
+    // token walk.
+    auto stage_in = [&](uint32_t t0, int cnt) {
+        const int tid = fresh_lane<true>(static_cast<int>(threadIdx.x));
+        constexpr int IB = ITEMS < 4 ? ITEMS : 4;  // items in flight per thread
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-            const float us = u[cc] * rho;
+        for (int b0 = 0; b0 < ITEMS; b0 += IB) {
+            float buf[IB][4];
 #pragma unroll
-            for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us, S[ri][cc]);
+            for (int ib = 0; ib < IB; ++ib) {
+                const int i = (b0 + ib) * NT + tid;
+                const int tk = i / PER_TOK, e = i - tk * PER_TOK;
+                if (b0 + ib < ITEMS && tk < cnt) {
+                    const RT* r = rec + static_cast<int64_t>(t0 + tk) * p.ring_tok;
+                    if (e < KV) {
+                        load_cols<4>(r + 4 * e, buf[ib]);
+                    } else if (e < KV + HW * UV) {
+                        const int f = e - KV, hh = f / UV;
+                        load_cols<4>(r + K + (m0 + hh) * V + 4 * (f - hh * UV), buf[ib]);
+                    } else {
+                        load_cols<1>(r + K + p.G * V + m0 + (e - KV - HW * UV), buf[ib]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int ib = 0; ib < IB; ++ib) {
+                const int i = (b0 + ib) * NT + tid;
+                const int tk = i / PER_TOK, e = i - tk * PER_TOK;
+                if (b0 + ib < ITEMS && tk < cnt) {
+                    float* d = stage + tk * FS::kTok;
+                    if (e < KV) {
+                        // a run of 4 stays inside one row group (R % 4 == 0 or no padding)
+                        *reinterpret_cast<float4*>(d + FS::kpos(4 * e)) =
+                            make_float4(buf[ib][0], buf[ib][1], buf[ib][2], buf[ib][3]);
+                    } else if (e < KV + HW * UV) {
+                        *reinterpret_cast<float4*>(d + FS::kK + 4 * (e - KV)) =
+                            make_float4(buf[ib][0], buf[ib][1], buf[ib][2], buf[ib][3]);
+                    } else {
+                        d[FS::kK + HW * V + (e - KV - HW * UV)] = buf[ib][0];
+                    }
+                }
+            }
         }
+        __syncthreads();
+    };
+    const int um = m - m0;  // this wave's head among the staged ones
+    const uint32_t tch = TCH;
+    stage_in(0, static_cast<int>(min(n, tch)));
+    float S[R][CPL];
+#pragma unroll
+    for (int ri = 0; ri < R; ++ri) widen_cols<CPL>(raw[ri], S[ri]);
+    float scale = 1.0f;
+    for (uint32_t t0 = 0;;) {
+        const int cnt = static_cast<int>(min(n - t0, tch));
+        for (int tk = 0; tk < cnt; ++tk) {
+            const float* d = stage + tk * FS::kTok;
+            const float a = d[FS::kK + HW * V + um];
+            float kr[R];
+            if constexpr (FS::kPad) {
+                read_rows<R>(d, kg, kr);
+            } else {
+#pragma unroll
+                for (int ri = 0; ri < R; ++ri) kr[ri] = d[kg * R + ri];
+            }
+            float u[CPL];
+            load_cols<CPL>(d + FS::kK + um * V + j0, u);
+            scale = decay_step<R, CPL>(S, scale * a);
+            const float rho = __builtin_amdgcn_rcpf(scale);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float us = u[cc] * rho;
+#pragma unroll
+                for (int ri = 0; ri < R; ++ri) S[ri][cc] = __builtin_fmaf(kr[ri], us, S[ri][cc]);
+            }
+        }
+        t0 += tch;
+        if (t0 >= n) break;
+        __syncthreads();  // every wave has read the stage
+        stage_in(t0, static_cast<int>(min(n - t0, tch)));
     }
 #pragma unroll
     for (int ri = 0; ri < R; ++ri) {
@@ -230,7 +293,13 @@ static hipError_t launch_fold_wpg(const FoldParams& p, int wpg, hipStream_t stre
 template <typename ST>
 static hipError_t launch_fold_st(const FoldParams& p, const LaunchShape& s, hipStream_t stream) {
     switch (s.K) {
-        case 128: return s.cpl == kFoldCpl ? launch_fold_wpg<128, kFoldCpl, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
+        case 128:
+            if (p.ring_bf16)
+                return s.cpl == kFoldCplBf16Ring
+                           ? launch_fold_rt<128, kFoldCplBf16Ring, ST, uint16_t>(p, s.wpg, stream)
+                           : hipErrorInvalidValue;
+            return s.cpl == kFoldCpl ? launch_fold_rt<128, kFoldCpl, ST, float>(p, s.wpg, stream)
+                                     : hipErrorInvalidValue;
         case 256: return s.cpl == 2 ? launch_fold_wpg<256, 2, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 64: return s.cpl == 8 ? launch_fold_wpg<64, 8, ST>(p, s.wpg, stream) : hipErrorInvalidValue;
         case 32: return s.cpl == 4 ? launch_fold_wpg<32, 4, ST>(p, s.wpg, stream) : hipErrorInvalidValue;

@@ -356,10 +356,11 @@ def test_launch_shape_independence():
     assert np.array_equal(st_a[s], st_b[s])
 
 
-@pytest.mark.parametrize("K", [128, 256])
-def test_fold_equals_forward_prefix_every_n(K):
-    ring_len = 6
-    lengths = [1, 6, 3, 9, 5]
+@pytest.mark.parametrize("K,ring_len", [(128, 6), (256, 6), (128, 19), (64, 19), (16, 19)])
+def test_fold_equals_forward_prefix_every_n(K, ring_len):
+    """fold(n) equals the forward pass over the first n tokens, bit for bit,
+    for every n; a ring longer than 8 tokens folds in several LDS stages."""
+    lengths = [1, 6, 3, 9, 5] if ring_len < 9 else [1, 19, 8, 20, 17]
     nk, nv, V = 2, 4, K
     w = P.small_packed(40, lengths, nk=nk, nv=nv, K=K, V=V, slots=7, state_dtype="bf16")
     stride = wl.ring_record_stride(nv // nk, K, V)
