@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--only decode,decode_bf16,prefill,verify,verify_bf16ring,gdp,
                             gdp_v256,gdp_betacols,conv,decode_small]
-                    [--no-cpu-baseline] [--copy-probe MiB]
+                    [--no-cpu-baseline] [--copy-probe MiB] [--verify-window L]
 
 Headline: the decode step (256 sequences x 1 token, nk=16, nv=32, K=V=128,
 bf16 state pool of 512 slots) through gdr_recurrence_fwd; `value` is decode
@@ -18,9 +18,14 @@ inputs and output, the ragged prefill (VALU-bound), the speculative verify +
 fold with a float32 and with a bf16 ring (HBM-bound), the Gated DeltaProduct
 decode with snapshots and the snapshot rollback (HBM-bound), and that decode
 with V = 256 (K != V) and with per-column beta; the Pass-1 causal Conv1d over
-the prefill's rows and over a decode step (HBM-bound).  The CPU baseline is
-the plain C oracle timed on the host on a bounded sample of the decode
-workload.
+the prefill's rows and over a decode step (HBM-bound); decode steps of 1, 4,
+16 and 64 sequences.  Each case also reports single-launch p10 / median / p90
+and the mean single launch of each rotation set.
+
+The CPU baseline is the plain C oracle timed on the host on whole decode
+batches, once on N threads (its independent (sequence, value head) items
+farmed over the host's cores; `cores` = N) and once on one thread
+(`threads_1`), with the CPU model from /proc/cpuinfo.
 """
 from __future__ import annotations
 
@@ -213,12 +218,12 @@ def case_prefill(torch, gdr, B, wl, rotations):
                 extra={"max_len": int(lens.max()), "lengths": lens.tolist()})
 
 
-def case_verify_fold(torch, gdr, B, wl, rotations, ring_bf16=False):
-    w = wl.verify_window()
-    suffix = ""
+def case_verify_fold(torch, gdr, B, wl, rotations, ring_bf16=False, fixed_len=None):
+    w = wl.verify_window(fixed_len=fixed_len)
+    suffix = "" if fixed_len is None else f"_len{fixed_len}"
     if ring_bf16:  # the same window with a bf16 ring (verify page, ring_dtype)
         w = dict(w, ring=np.zeros(w["ring"].shape, np.uint16))
-        suffix = "_bf16ring"
+        suffix += "_bf16ring"
     ring_es = 2 if ring_bf16 else 4
     lens = np.diff(w["row_offsets"].astype(np.int64))
     ring_len = w["ring"].shape[2]
@@ -349,8 +354,9 @@ def time_case(torch, case, steps, warmup):
 
 def launch_spread(torch, case, n):
     """p10 / median / p90 of single launches (one HIP event pair around each, on
-    the launch stream), taken after the timed region; the reported rate comes
-    from the back-to-back timed region, not from these."""
+    the launch stream), taken after the timed region, and the mean single
+    launch of each rotation set (the spread across buffer sets); the reported
+    rate comes from the back-to-back timed region, not from these."""
     stream = torch.cuda.current_stream()
     m = len(case.launches)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -360,8 +366,10 @@ def launch_spread(torch, case, n):
         case.launches[i % m]()
         b.record(stream)
     torch.cuda.synchronize()
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-    return [round(us[n // 10], 2), round(us[n // 2], 2), round(us[(9 * n) // 10], 2)]
+    times = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    by_set = [round(float(np.mean(times[j::m])), 2) for j in range(min(m, n))]
+    us = sorted(times)
+    return [round(us[n // 10], 2), round(us[n // 2], 2), round(us[(9 * n) // 10], 2)], by_set
 
 
 def summarize(case, ms_per_launch):
@@ -476,6 +484,9 @@ def main():
                                       "gdp_v256,gdp_betacols,conv,decode_small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0)
+    ap.add_argument("--verify-window", type=int, default=0,
+                    help="with --only verify: every window of this length (1-12) instead of "
+                         "uniform in [1, 12]")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: every (sequence, value head) recurrence is "
@@ -500,7 +511,8 @@ def main():
     if "prefill" in only:
         cases.append(case_prefill(torch, gdr, B, wl, 2))
     if "verify" in only:
-        cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations))
+        cases.extend(case_verify_fold(torch, gdr, B, wl, args.rotations,
+                                      fixed_len=args.verify_window or None))
     if "conv" in only:
         cases.append(case_conv(torch, gdr, B, wl, args.rotations, decode=True))
         cases.append(case_conv(torch, gdr, B, wl, 2, decode=False))
@@ -527,8 +539,9 @@ def main():
         if "max_len" in results[c.name]:  # the token-serial critical path of the longest row
             results[c.name]["ns_per_step_of_longest_row"] = round(
                 ms * 1e6 / results[c.name]["max_len"], 1)
-        results[c.name]["single_launch_us_p10_p50_p90"] = launch_spread(
-            torch, c, min(steps, 100 if c.name != "prefill_8x4096" else 5))
+        spread, by_set = launch_spread(torch, c, min(steps, 100 if c.name != "prefill_8x4096" else 5))
+        results[c.name]["single_launch_us_p10_p50_p90"] = spread
+        results[c.name]["single_launch_us_mean_by_set"] = by_set
         print(f"# {c.name}: {json.dumps(results[c.name])}", file=sys.stderr, flush=True)
         if c.name == "decode_256x1":
             head = (c, ms, steps)

@@ -118,13 +118,16 @@ def ragged_prefill(seed: int = 1002, batch: int = 8, max_len: int = 4096, slots:
 
 
 def verify_window(seed: int = 1003, batch: int = 64, max_window: int = 12, ring_len: int = 8,
-                  slots: int = 128):
+                  slots: int = 128, fixed_len: int | None = None):
     """Speculative verify plus fold: 64 rows with windows uniform in [1, 12],
     ring_len 8, float32 ring and bf16 pool of 128 slots each; the accepted
     count is uniform in [0, len] for rows that fit the ring and the full
-    length for rows that do not (those rows commit during verify)."""
+    length for rows that do not (those rows commit during verify).  With
+    fixed_len every window has that length (instruction-count fits)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lengths = rng.integers(1, max_window + 1, size=batch)
+    if fixed_len is not None:
+        lengths = np.full(batch, fixed_len, dtype=lengths.dtype)
     w = packed_inputs(rng, lengths, nk=16, nv=32, K=128, V=128, slots=slots,
                       state_dtype="bf16", state_sigma=0.05)
     group = 32 // 16
