@@ -356,7 +356,7 @@ def test_launch_shape_independence():
     assert np.array_equal(st_a[s], st_b[s])
 
 
-@pytest.mark.parametrize("K,ring_len", [(128, 6), (256, 6), (128, 19), (64, 19), (16, 19)])
+@pytest.mark.parametrize("K,ring_len", [(128, 6), (256, 6), (128, 19), (256, 19), (64, 19), (16, 19)])
 def test_fold_equals_forward_prefix_every_n(K, ring_len):
     """fold(n) equals the forward pass over the first n tokens, bit for bit,
     for every n; a ring longer than 8 tokens folds in several LDS stages."""
@@ -580,6 +580,43 @@ def test_bf16_ring_verify_and_fold():
     ties = H.assert_state_close(fold_b[sl], fold_r[sl], "bf16-ring fold state", unr_f[sl])
     n_fit = int((lens <= ring_len).sum())
     say(f"bf16 ring: {n_fit} rows folded, fold ties {ties}")
+
+
+@pytest.mark.parametrize("K", [16, 128, 256])
+def test_bf16_ring_fold_multi_pass(K):
+    """A bf16 ring of 19 tokens folded in several LDS passes: for every n the
+    fold equals the fold of the widened float32 records bit for bit (at K = 128
+    the two run different tilings: 8 and 4 columns per lane), and the full
+    accepted prefixes match the oracle's bf16-ring fold within tolerance."""
+    ring_len = 19
+    lengths = [1, 19, 8, 20, 17]
+    nk, nv = 2, 4
+    w = P.small_packed(41, lengths, nk=nk, nv=nv, K=K, V=K, slots=7, state_dtype="bf16")
+    stride = wl.ring_record_stride(nv // nk, K, K)
+    ring0 = np.zeros((5, nk, ring_len, stride), np.uint16)
+    w["ring_slot_idx"] = np.array([3, 0, 4, 1, 2], np.uint32)
+    w["ring"] = ring0
+    say(f"bf16 ring fold in passes: K={K} ring_len {ring_len} lengths {lengths}")
+    _, st_v, ring_b = H.gpu_verify(w)
+    ring_w = np.ascontiguousarray(wl.bf16_bits_to_f32(ring_b))
+    for n in range(0, ring_len + 1):
+        acc = np.array([min(n, L) if L <= ring_len else L for L in lengths], np.uint32)
+        fold_b = H.gpu_fold(w, st_v, ring_b, acc)
+        fold_w = H.gpu_fold(w, st_v, ring_w, acc)
+        assert np.array_equal(fold_b, fold_w), (K, n)
+    acc = np.array([L if L <= ring_len else L for L in lengths], np.uint32)
+    args = {k: w[k] for k in ("qkv", "decay", "beta", "slot_idx", "row_offsets",
+                              "num_value_heads", "num_key_heads", "ring_slot_idx")}
+    _, st_r, ring_r = oracle.recurrence_verify_ring(**args, state=w["state"], ring=ring0)
+    _, unr_v, ring_ru = oracle.recurrence_verify_ring(**args, state=H.f32_pool(w["state"]),
+                                                      ring=ring0)
+    fold_kw = dict(slot_idx=w["slot_idx"], ring_slot_idx=w["ring_slot_idx"], accepted=acc,
+                   num_value_heads=nv, num_key_heads=nk)
+    fold_r = oracle.state_fold(state=st_r, ring=ring_r, **fold_kw)
+    unr_f = oracle.state_fold(state=unr_v, ring=ring_ru, **fold_kw)
+    fold_g = H.gpu_fold(w, st_v, ring_b, acc)
+    sl = w["slot_idx"].astype(np.int64)
+    H.assert_state_close(fold_g[sl], fold_r[sl], f"bf16-ring fold K={K}", unr_f[sl])
 
 
 # ------------------------------------------------------- bf16 work dtype ---
