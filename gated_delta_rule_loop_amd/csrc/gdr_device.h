@@ -333,11 +333,11 @@ __device__ __forceinline__ void widen_cols(const RawCols<uint16_t, CPL>& r, floa
     }
 }
 
-// The lane index as a value the compiler may not hoist (when HIDE): the
-// stage code derives addresses from it, and computing them where they are
-// used (once per stage) keeps them out of the registers that the token loop
-// needs.  Only the short-row shapes, whose token loop fills the register
-// budget, ask for it.
+// The lane index as a value the compiler may not hoist (when HIDE): staging
+// code derives addresses from it, and computing them where they are used
+// (once per stage) keeps them out of the registers that the token loop
+// needs.  The short-row shapes, whose token loop fills the register budget,
+// and the fold's record staging ask for it.
 template <bool HIDE>
 __device__ __forceinline__ int fresh_lane(int lane) {
     if constexpr (HIDE) asm volatile("" : "+v"(lane));
