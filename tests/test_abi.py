@@ -164,6 +164,11 @@ def test_fused_argument_checks():
     st = T([5, 4, 16, 16], B.GDR_DTYPE_BF16)
     assert call(state=st, inter=T([5, 3, 4, 16, 16], B.GDR_DTYPE_F32)) == -2  # dtype mismatch
     assert call(state=st, idx=T([3], B.GDR_DTYPE_I32)) == -1       # indices must be [N]
+    # q and k are read in aligned 4-element runs: their rows need 16-byte strides
+    odd = T([2, 3, 2, 16], stride=[108, 36, 18, 1])
+    assert call(q=odd) == -2 and "multiple of 4" in B.gdr_last_error_message()
+    assert call(k=odd) == -2 and "multiple of 4" in B.gdr_last_error_message()
+    assert call(q=T([2, 3, 2, 16], stride=[96, 32, 16, 2])) == -2  # innermost not unit
 
 
 def test_output_shape_helper():
