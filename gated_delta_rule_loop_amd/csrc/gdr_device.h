@@ -1034,18 +1034,18 @@ struct Rec {
         return __ballot(!ok) == 0;
     }
 
-    // The tokens of a multi-token stage: as run_chunk, with the next token's
-    // retrieval computed unconditionally in the same register pass as this
-    // token's read-out (after the stage's last token it reads a k_hat slot
-    // that holds no token of the row and the value is discarded), and the
-    // decay range test made once per stage when CHECK is false.  x holds the
-    // retrieval of the current token: per column (row groups low), or spread
-    // (row groups high, see sum_cols_spread).
-    static constexpr int kX = kSpreadOut ? kSpread<CPL> : CPL;
+    // The tokens of a multi-token stage (the row-groups-low layout of the
+    // long-row shapes): as run_chunk, with the next token's retrieval computed
+    // unconditionally in the same register pass as this token's read-out
+    // (after the stage's last token it reads a k_hat slot that holds no token
+    // of the row and the value is discarded), and the decay range test made
+    // once per stage when CHECK is false.  x holds the retrieval of the
+    // current token, one value per column.
     template <bool CHECK, bool REC, bool SNAP, bool BC>
     __device__ static void stage_tokens(const RecParams& p, const Item& it, int tc, int Lc,
                                         const float* B, float (&S)[R][CPL], float& scale,
-                                        float (&kr)[R], float (&x)[kX], int w, int lane) {
+                                        float (&kr)[R], float (&x)[CPL], int w, int lane) {
+        static_assert(KG_LOW, "stage_tokens serves the row-groups-low layout");
         const int kg = row_group(lane);
         const int vc = col_chunk(lane) * CPL;
         WT* outp = out_ptr(p, it) + static_cast<int64_t>(tc) * p.o_tok;
@@ -1062,34 +1062,22 @@ struct Rec {
                    static_cast<int64_t>(it.hv) * p.snap_head + it.j0;
         }
         int snap_i = SNAP ? tc / p.spt : 0;
-        // spread form: this lane holds the totals of columns vc + scol(i)
-        const int r16 = lane >> 4;
-        auto scol = [&](int i) { return (CPL == 2 ? (r16 & 1) : r16) + 4 * i; };
-        const bool spread_lead = (lane & 8) == 0 && (CPL != 2 || lane < 32);
         for (int tau = 0; tau < Lc; ++tau) {
             const float a = B[OFF_A + w * C + tau];
             const float b = BC ? 1.0f : B[OFF_B + w * C + tau];
             const float cn = scale * a;
-            float u[kX];  // u of the lane's columns (spread: of its spread columns)
+            float u[CPL];
 #pragma unroll
-            for (int i = 0; i < kX; ++i) {
-                const int cc = kSpreadOut ? scol(i) : i;
+            for (int cc = 0; cc < CPL; ++cc) {
                 const float vv = B[OFF_V + w * VTOT + tau * BV + vc + cc];
                 const float be = BC ? B[OFF_BV + w * VTOT + tau * BV + vc + cc] : b;
-                u[i] = be * (vv - cn * x[i]);
+                u[cc] = be * (vv - cn * x[cc]);
             }
             scale = CHECK ? decay_step<R, CPL>(S, cn) : cn;
             const float rho = __builtin_amdgcn_rcpf(scale);
             float us[CPL];
-            if constexpr (kSpreadOut) {
-                float us_s[kX];
 #pragma unroll
-                for (int i = 0; i < kX; ++i) us_s[i] = u[i] * rho;
-                spread_to_all<CPL>(us_s, us);
-            } else {
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) us[cc] = u[cc] * rho;
-            }
+            for (int cc = 0; cc < CPL; ++cc) us[cc] = u[cc] * rho;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
@@ -1098,36 +1086,18 @@ struct Rec {
             read_rows<R>(B + OFF_Q + tau * KP, kg, qr);
             read_rows<R>(B + OFF_K + (tau + 1) * KP, kg, kr);
             dot_rows2(S, qr, kr, o, xk);
-            if constexpr (kSpreadOut) {
-                float y[kX];
-                sum_cols_spread<CPL>(o, y);
-                sum_cols_spread<CPL>(xk, x);
-                if (spread_lead) {
 #pragma unroll
-                    for (int i = 0; i < kX; ++i) {
-                        const float val = scale * y[i];
-                        store_cols<1>(outp + scol(i), &val);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    o[cc] = scale * sum_row_groups<true>(o[cc]);
-                    x[cc] = sum_row_groups<true>(xk[cc]);
-                }
-                // every lane holds its columns' totals: the 8 lanes of a
-                // column store the same bits to the same address
-                store_cols<CPL>(outp, o);
+            for (int cc = 0; cc < CPL; ++cc) {
+                o[cc] = scale * sum_row_groups<true>(o[cc]);
+                x[cc] = sum_row_groups<true>(xk[cc]);
             }
+            // every lane holds its columns' totals: the 8 lanes of a column
+            // store the same bits to the same address
+            store_cols<CPL>(outp, o);
             outp += p.o_tok;
             if (REC && it.record) {
                 const int64_t ru = rec + K + it.m * V + it.j0;
-                if constexpr (kSpreadOut) {
-                    if (spread_lead) {
-#pragma unroll
-                        for (int i = 0; i < kX; ++i) ring_put(p, ru + scol(i), u[i]);
-                    }
-                } else if (kg == 0) {
+                if (kg == 0) {
                     if (p.ring_bf16)
                         store_cols<CPL>(static_cast<uint16_t*>(p.ring) + ru, u);
                     else
@@ -1147,25 +1117,21 @@ struct Rec {
         }
     }
 
-    // A multi-token stage: the retrieval of its first token, the stage-wide
-    // decay range test, then the tokens.
+    // A multi-token stage of the row-groups-low layout: the retrieval of its
+    // first token, the stage-wide decay range test, then the tokens.
     template <bool REC, bool SNAP, bool BC>
     __device__ static void run_stage(const RecParams& p, const Item& it, int c, const float* B,
                                      float (&S)[R][CPL], float& scale, int w, int lane) {
-        static_assert(C > 1, "multi-token stages");
+        static_assert(C > 1 && KG_LOW, "multi-token stages of the row-groups-low layout");
         const int kg = row_group(lane);
         const int tc = c * C;
         const int Lc = __builtin_amdgcn_readfirstlane(min(C, it.L - tc));
-        float kr[R], x[kX];
+        float kr[R], x[CPL];
         read_rows<R>(B + OFF_K, kg, kr);
         float xc[CPL];
         dot_rows<R, CPL>(S, kr, xc);
-        if constexpr (kSpreadOut) {
-            sum_cols_spread<CPL>(xc, x);
-        } else {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<true>(xc[cc]);
-        }
+        for (int cc = 0; cc < CPL; ++cc) x[cc] = sum_row_groups<true>(xc[cc]);
         if (stage_in_range(B + OFF_A + w * C, Lc, scale, lane))
             stage_tokens<false, REC, SNAP, BC>(p, it, tc, Lc, B, S, scale, kr, x, w, lane);
         else
