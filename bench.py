@@ -52,7 +52,7 @@ FLOPS_PER_TOKEN_HEAD_ELEM = 7    # decay 1, S^T k 2, rank-1 write 2, S^T q 2 per
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("gdr_device.h", "gdr_kernels.hip", "gdr_rec_table.hip", "gdr_api.cpp",
-              "gdr_internal.h"):
+              "gdr_internal.h", "gdr_fastdiv.h"):
         with open(os.path.join(ROOT, "gated_delta_rule_loop_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -5,23 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdr_fastdiv.h"
+
 namespace gdr {
 
 constexpr uint32_t kPadSlot = 0xFFFFFFFFu;
 
-// Division of a non-negative int32 below 2^31 by a divisor fixed for a
-// launch, as a multiply: q = (mulhi(x, mul) + x) >> shift, with shift =
-// ceil(log2 d) and mul = floor(2^32 (2^shift - d) / d) + 1 (exact for every
-// x < 2^31; computed on the host).
-struct FastDiv {
-    uint32_t mul, shift;
-};
-inline FastDiv make_fastdiv(uint32_t d) {
-    uint32_t s = 0;
-    while ((uint64_t{1} << s) < d) ++s;
-    const uint64_t m = ((uint64_t{1} << 32) * ((uint64_t{1} << s) - d)) / d + 1;
-    return FastDiv{static_cast<uint32_t>(m), s};
-}
 
 // One launch of the recurrence kernel.  All strides are in elements.
 // A token tensor X of row r, sequence-local token t and head hd lives at
